@@ -1,0 +1,282 @@
+"""Benchmark of the sparse-attention step on one MI355X.
+
+Workload (default): speculative-verify decode at 64k context -- 64 requests x 4 query rows,
+context 65,536, paged 64-token blocks with a seeded random block table, indexer 64 heads x
+128 on the 132-byte FP8 cache, top-2048, MLA 128 heads on the 656-byte FP8 latent cache,
+SSMax s = 0.3; one RoPE layer and one NoPE layer per step.  Inputs are seeded synthetic
+data drawn on the GPU and resident in HBM before timing starts.
+
+One step = for each layer: indexer scores -> exact top-k -> sparse MLA (the three entry
+points the fused entry chains), timed with HIP events on the launch stream.
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s + achieved HBM GB/s, sparse MLA+DSA at 64k context"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = verify at 64k)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU budget of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused entry instead (no per-kernel events)")
+    return ap.parse_args()
+
+
+def kernel_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_attention_decode_dsa_amd", "csrc", KERNEL_SOURCES[name])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_work(case):
+    """Per layer: indexer bytes (keys read once per request + queries), MLA bytes (selected
+    latent rows + q + o) and MLA FLOPs, from the workload's shape."""
+    b = case.batch
+    seq = b.seq_lens.cpu().tolist()
+    T, Hi, H = b.total_q, case.idx_heads, case.mla_heads
+    qpos = b.q_pos.cpu().tolist()
+    out = {}
+    for d in case.layers:
+        k = d["top_k"]
+        nsel = [min(k, p + 1) for p in qpos]
+        idx_bytes = 0
+        if d["topk_source_layer"] < 0:
+            idx_bytes = sum(n * 132 for n in seq) + T * Hi * (128 + 8)
+        rope = d["rope_dim"]
+        row = 656 if rope else 528
+        mla_bytes = sum(nsel) * row + T * H * (512 + rope) * 2 + T * H * 512 * 2
+        mla_flops = sum(nsel) * 2 * H * (1024 + rope)
+        idx_flops = sum(n * 2 * Hi * 128 * q for n, q in
+                        zip(seq, [b.q_start[i + 1].item() - b.q_start[i].item()
+                                  for i in range(b.batch)])) if d["topk_source_layer"] < 0 else 0
+        out[d["layer"]] = dict(idx_bytes=idx_bytes, idx_flops=idx_flops, mla_bytes=mla_bytes,
+                               mla_flops=mla_flops)
+    return out
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current
+    kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except Exception:
+        return None
+    if t.get("source_sha256_16") != kernel_hash(kernel):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload's query rows."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from tests.compare import t_np
+
+    b = case.batch
+    bs = b.block_size
+    q_start = b.q_start.cpu().numpy()
+    rows_done = 0
+    t0 = time.perf_counter()
+    sample = []
+    r = 0
+    # whole requests, all their rows, all layers, until the budget is spent
+    for req in range(b.batch):
+        if time.perf_counter() - t0 > budget_s and rows_done:
+            break
+        nblk = (int(b.seq_lens[req].item()) + bs - 1) // bs
+        blocks = b.block_table[req, :nblk].long()
+        seqs = O.Seqs(np.array([int(b.seq_lens[req].item())]), np.array([0, int(q_start[req + 1] - q_start[req])]),
+                      b.q_pos[q_start[req]:q_start[req + 1]].cpu().numpy().astype(np.int64),
+                      np.arange(nblk)[None, :], bs)
+        rows = slice(int(q_start[req]), int(q_start[req + 1]))
+        lat, idxp = {}, {}
+        for d in case.layers:
+            li = case.inputs[d["layer"]]
+            if li.lat_pool is not None:
+                lat[d["layer"]] = t_np(li.lat_pool[blocks])
+            if li.idx_pool is not None:
+                idxp[d["layer"]] = t_np(li.idx_pool[blocks])
+        store = {}
+        t_req = time.perf_counter()
+        for d in case.layers:
+            li = case.inputs[d["layer"]]
+            L = O.Layer(d["layer"], d["kv_sharing_target_layer"], d["topk_source_layer"],
+                        d["rope_dim"], d["top_k"], d["softmax_scale"], d["ssmax_s"],
+                        d["idx_ssmax_s"])
+            O.layer_step(L, seqs, case.fmt, lat, idxp,
+                         None if li.q_idx is None else t_np(li.q_idx[rows]),
+                         None if li.q_idx_scale is None else t_np(li.q_idx_scale[rows]),
+                         None if li.w_idx is None else t_np(li.w_idx[rows]),
+                         t_np(li.q_mla[rows]), store, ld=int(b.max_seq_len))
+        sample.append(time.perf_counter() - t_req)
+        rows_done += seqs.total_q
+    elapsed = sum(sample)
+    cores = None
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": rows_done / elapsed, "unit": "query-tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{rows_done} query rows ({len(sample)} whole requests), every layer of "
+                      f"the step, fp64 numpy oracle; {elapsed:.1f} s of compute"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from sparse_attention_decode_dsa_amd import ml4dsa  # noqa: F401 (fails loudly if unbuilt)
+    from sparse_attention_decode_dsa_amd import synth
+    from sparse_attention_decode_dsa_amd.runner import CaseRunner
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    print(f"[bench] generating workload {args.config} on {dev}", file=sys.stderr, flush=True)
+    case = synth.config(args.config, device=dev)
+    torch.cuda.synchronize()
+    run = CaseRunner(case)
+    layers = [d["layer"] for d in case.layers]
+    print(f"[bench] {case.name}: rows {case.batch.total_q}, max context "
+          f"{case.batch.max_seq_len}, layers {layers}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run.run_step(fused=args.fused)
+    torch.cuda.synchronize()
+    assert run.fault_bits() == 0, "fault word set during warm-up"
+
+    K = args.steps
+    ev = {l: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+          for l in layers}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(K):
+        for l in layers:
+            if args.fused:
+                run.run_layer_fused(l)
+            else:
+                run.run_layer_split(l, events=ev[l][k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / K
+    assert run.fault_bits() == 0, "fault word set during timing"
+
+    work = algorithmic_work(case)
+    T = case.batch.total_q
+    per = {}
+    if not args.fused:
+        for l in layers:
+            d = [x for x in case.layers if x["layer"] == l][0]
+            own = d["topk_source_layer"] < 0
+            per[l] = {
+                "indexer_us": 1e3 * sum(ev[l][k][0].elapsed_time(ev[l][k][1]) for k in range(K)) / K if own else 0.0,
+                "topk_us": 1e3 * sum(ev[l][k][1].elapsed_time(ev[l][k][2]) for k in range(K)) / K if own else 0.0,
+                "mla_us": 1e3 * sum(ev[l][k][2].elapsed_time(ev[l][k][3]) for k in range(K)) / K,
+            }
+    step_bytes = sum(w["idx_bytes"] + w["mla_bytes"] for w in work.values())
+    result = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (indexer MFMA) + bf16 (MLA MFMA), fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {
+            "workload": case.name,
+            "batch": case.batch.batch, "query_rows": T, "context": case.batch.max_seq_len,
+            "block_size": case.batch.block_size, "indexer_heads": case.idx_heads,
+            "mla_heads": case.mla_heads, "top_k": case.layers[0]["top_k"],
+            "layers_per_step": len(layers),
+            "layer_modes": [{k: d[k] for k in ("layer", "rope_dim", "kv_sharing_target_layer",
+                                                "topk_source_layer", "ssmax_s")}
+                            for d in case.layers],
+            "us_per_layer_step": 1e3 * ms / len(layers),
+            "algorithmic_GBps": step_bytes / (ms * 1e-3) / 1e9,
+            "per_layer_us": per,
+            "wall_s": wall,
+        },
+    }
+    if per:
+        # dominant kernel: the largest summed device time over the step
+        tot = {"indexer": sum(p["indexer_us"] for p in per.values()),
+               "topk": sum(p["topk_us"] for p in per.values()),
+               "mla": sum(p["mla_us"] for p in per.values())}
+        dom = max(tot, key=tot.get)
+        l0 = layers[0]
+        if dom == "indexer":
+            us = per[l0]["indexer_us"]
+            ach = work[l0]["idx_bytes"] / (us * 1e-6) / 1e9
+            roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": ach / PEAK_HBM_GBS}
+        elif dom == "mla":
+            us = per[l0]["mla_us"]
+            ach = work[l0]["mla_flops"] / (us * 1e-6) / 1e12
+            roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": ach / PEAK_BF16_TFLOPS}
+        else:
+            us = per[l0]["topk_us"]
+            ach = (T * case.batch.max_seq_len * 4) / (us * 1e-6) / 1e9
+            roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": ach / PEAK_HBM_GBS}
+        roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8", "topk": "k_topk_row"}[dom]
+        roof["layer"] = l0
+        roof["avg_launch_us"] = us
+        roof["traffic"] = load_traffic(dom)
+        result["roofline"] = roof
+    if args.cpu_seconds > 0:
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["config"]["calib_copy_bytes"] = n
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * ml4dsa.h -- C ABI of the MI355X (gfx950) library for the DeepSeek-style sparse-attention
+ * step of Mistral Large 4: DSA indexer scores -> exact top-k -> sparse MLA over the selected
+ * latent rows, with NoPE, shared-indexer and KV-sharing-consumer layers.
+ *
+ * Pages cited (by title and section):
+ *   [blog]   "vLLM 首日支持 Mistral Large 4：1T 参数 MoE 多模态模型" (best2ai.com translation of
+ *            the vLLM day-0 post)
+ *   [recipe] "mistralai/Mistral-Large-4-1T-A52B — vLLM serving recipe" (recipes.vllm.ai)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer,
+ *     including workspace and the fault word; the library keeps no pointer after a call
+ *     returns.  Work is enqueued asynchronously on `stream` (NULL = the default stream); no
+ *     entry point synchronises except ml4_fault_query.
+ *   - Return value: ML4_OK (0) or a negative ml4_status.  Host-side validation is
+ *     default-deny [blog, ROCm implementation details › 专用解码 / default-deny: refuse and
+ *     list every reason]: every argument check is evaluated, every failure is listed, one
+ *     per line, in the thread-local ml4_last_error(), and nothing is launched.
+ *   - Device-side problems (a block id outside the pool, a top-k entry outside [0, q_pos],
+ *     a NaN score, q_pos outside [0, seq_len)) set bits in the caller's sticky fault word
+ *     [blog, ROCm implementation details › Fail-stop: a sticky fault word checked after
+ *     each forward] and the affected key or row is masked; kernels always run to
+ *     completion.  ml4_fault_query() reads the word.
+ *   - The library allocates no device memory and never calls hipMalloc/hipFree.
+ */
+#ifndef ML4DSA_H
+#define ML4DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
+
+#define ML4_ABI_VERSION 1
+
+enum ml4_status {
+  ML4_OK = 0,
+  ML4_E_INVALID = -1,       /* an argument is out of its documented range       */
+  ML4_E_UNSUPPORTED = -2,   /* a valid combination this build does not provide   */
+  ML4_E_WORKSPACE = -3,     /* ws_bytes below ml4_workspace_bytes()              */
+  ML4_E_LAUNCH = -4,        /* the HIP runtime refused a launch                  */
+  ML4_E_DEVICE_FAULT = -5   /* ml4_fault_query found fault bits set              */
+};
+
+enum ml4_dtype { ML4_F32 = 0, ML4_BF16 = 1, ML4_FP8_E4M3 = 2 };
+
+/* Indexer cache row formats.  [blog, ROCm implementation details › AITER 上的 DSA 索引器:
+ * FP8 indexer keys with a single scale per key, 132 bytes per token per indexer layer] */
+enum ml4_index_format {
+  ML4_IDX_F32 = 0,      /* 128 x fp32 = 512 B per token; no key scale (fp32 test format)    */
+  ML4_IDX_FP8_132 = 1   /* [128 x e4m3 (OCP E4M3FN)][fp32 key scale] = 132 B per token      */
+};
+
+/* Latent cache row formats.  [blog, Implementation details › 稀疏 MLA + DSA indexer (latent
+ * cache in fp8_ds_mla); ROCm implementation details › FP8 潜在缓存 (656 B per token per
+ * layer)]; KV LoRA rank 512 and RoPE dim 64 [blog, Highlights]. */
+enum ml4_latent_format {
+  ML4_LAT_F32 = 0,      /* [512 x fp32 latent][64 x fp32 RoPE] = 2,304 B (fp32 test format) */
+  ML4_LAT_FP8_656 = 1   /* [512 x e4m3][4 x fp32 scale, one per 128][64 x bf16 RoPE] = 656 B */
+};
+
+#define ML4_IDX_DIM 128
+#define ML4_KV_LORA 512
+#define ML4_ROPE_DIM 64
+#define ML4_IDX_ROW_FP8 132
+#define ML4_LAT_ROW_FP8 656
+#define ML4_MAX_TOPK 2048
+
+enum ml4_fault_bits {
+  ML4_FAULT_BLOCK_ID = 1u << 0,    /* block_table entry outside [0, num_blocks)           */
+  ML4_FAULT_TOPK_INDEX = 1u << 1,  /* topk entry outside [0, q_pos] or topk_len > top_k    */
+  ML4_FAULT_NAN_SCORE = 1u << 2,   /* a candidate score was NaN (ranked below -inf)        */
+  ML4_FAULT_QPOS = 1u << 3         /* q_pos outside [0, seq_len) or > max_seq_len - 1      */
+};
+
+/* A batch of requests.  [host] struct; the arrays are device memory.
+ * Request b owns query rows q_start[b] .. q_start[b+1]-1; row r sees logical key positions
+ * 0 .. q_pos[r] (a query sees its own key).  Logical position t of request b lives in cache
+ * slot block_table[b][t / block_size] * block_size + t % block_size [blog, ROCm
+ * implementation details › AITER 上的稀疏 MLA: top-k positions become global cache slots,
+ * one entry per query token]. */
+typedef struct {
+  int32_t batch;               /* requests B >= 1                                           */
+  int32_t total_q;             /* query rows = q_start[B] >= 1                              */
+  int32_t max_seq_len;         /* host bound: seq_lens[b] <= max_seq_len (sizes grids)     */
+  int32_t max_q_per_seq;       /* host bound: q_start[b+1] - q_start[b] <= max_q_per_seq   */
+  int32_t block_size;          /* tokens per block: power of two, 16 .. 65536 (pages: 64)  */
+  int32_t max_blocks_per_seq;  /* row stride of block_table, >= ceil(max_seq_len/bs)       */
+  const int32_t* seq_lens;     /* [B]   cached tokens, including this step's               */
+  const int32_t* q_start;      /* [B+1] query-row offsets, q_start[0] = 0                   */
+  const int32_t* q_pos;        /* [total_q] absolute position of each query row            */
+  const int32_t* block_table;  /* [B][max_blocks_per_seq] physical block ids               */
+} ml4_seqs;
+
+/* One layer's cache: pool = [num_blocks][block_size][row bytes of `format`], 16-B aligned. */
+typedef struct {
+  const void* pool;
+  int64_t num_blocks;
+  int32_t format;              /* ml4_index_format or ml4_latent_format                     */
+} ml4_cache;
+
+/*
+ * ml4_indexer_score -- DSA indexer scores over every visible cached key.
+ * [blog, Highlights (DSA sparse indexer); Implementation details › 稀疏 MLA + DSA indexer
+ * (FP8 indexer cache; the indexer has its own SSMax); ROCm implementation details › AITER 上的
+ * DSA 索引器 (132-B FP8 keys, one scale per key; paged decode scores and prefill scores)]
+ *   scores[r][t] = m_r * ks[t] * sum_h w[r][h] * qs[r][h] * ReLU(sum_d q[r][h][d] * k[t][d])
+ *   for 0 <= t <= q_pos[r];  -inf for q_pos[r] < t < max_seq_len; columns >= max_seq_len are
+ *   not written.  m_r = ssmax_s * ln(q_pos[r] + 1) when ssmax_s > 0, else 1.
+ *   q        [total_q][n_heads][128]: e4m3 codes (ML4_FP8_E4M3) with an ML4_IDX_FP8_132
+ *            cache, or fp32 (ML4_F32) with an ML4_IDX_F32 cache; 16-B aligned.
+ *   q_scale  [total_q][n_heads] fp32, or NULL (= 1).   w [total_q][n_heads] fp32.
+ *   n_heads  multiple of 16, 16 .. 64.   ld_scores >= max_seq_len, multiple of 4.
+ * Decode rows stream the paged cache; rows of one request share each key load (speculative
+ * verify, prefill).  fp32 accumulation; the fp8 products are exact.
+ */
+int ml4_indexer_score(const ml4_seqs* s, const ml4_cache* idx_cache, const void* q,
+                      int32_t q_dtype, const float* q_scale, const float* w, int32_t n_heads,
+                      float ssmax_s, float* scores, int64_t ld_scores, uint32_t* fault,
+                      hipStream_t stream);
+
+/*
+ * ml4_topk_select -- exact top-k of each row's visible scores.
+ * [blog, ROCm implementation details › 专用解码 (exact top-2048); Long context › DCP (a
+ * stable top-k merge; radix select over packed (score, id) candidates; top-k compaction:
+ * -1 padded slots bounded by topk_length); recipe/blog: index_topk]
+ *   Candidates t in [0, q_pos[r]] of scores[r][*].  Order: higher score first, then lower t;
+ *   -0 == +0; NaN ranks below -inf (and sets ML4_FAULT_NAN_SCORE).
+ *   topk_idx [total_q][top_k] int32: the selected positions in ascending t, then -1.
+ *   topk_len [total_q] int32 = min(top_k, q_pos[r] + 1).
+ *   1 <= top_k <= 2048.  ws: ml4_workspace_bytes(ML4_ENTRY_TOPK, ...) bytes (may be 0).
+ * Integer work on the order-preserving u32 image of each fp32 score: deterministic.
+ */
+int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, int32_t top_k,
+                    int32_t* topk_idx, int32_t* topk_len, void* ws, size_t ws_bytes,
+                    uint32_t* fault, hipStream_t stream);
+
+/*
+ * ml4_sparse_mla_decode -- MLA attention over the selected latent rows.
+ * [blog, Highlights (MLA, KV LoRA rank 512, RoPE dim 64, top 2048 keys per query);
+ * Implementation details › 稀疏 MLA + DSA indexer (sparse MLA over the fp8_ds_mla latent
+ * cache); › NoPE、SSMax 和 LeRoPE (NoPE = MLA with RoPE dim 0, same kernel and layout; SSMax
+ * logit scaling); › 跨层 KV 共享 (a consumer layer reads its target layer's cache);
+ * Long context › DCP (partial attention merged by log-sum-exp)]
+ *   For row r, head h, over its valid selected positions t (topk_idx[r][0..topk_len[r])):
+ *     l_t = sigma_r * (qa[r][h] . c_t + qr[r][h] . kr_t),
+ *     sigma_r = softmax_scale * (ssmax_s > 0 ? ssmax_s * ln(q_pos[r] + 1) : 1),
+ *     out[r][h] = sum_t softmax(l)_t * c_t   (the latent row is key and value),
+ *     lse[r][h] = natural-log log-sum-exp of l (or -inf when topk_len[r] == 0, out = 0).
+ *   kv       the latent cache to read: the layer's own, or the target's for a consumer.
+ *   q        [total_q][n_heads][512 + rope_dim]: bf16 with ML4_LAT_FP8_656, fp32 with
+ *            ML4_LAT_F32.   n_heads: multiple of 16, 16 .. 128.   rope_dim: 64, or 0 (NoPE:
+ *            the RoPE bytes are never read).
+ *   out      [total_q][n_heads][512]: bf16 (fp8 cache) or fp32 (fp32 cache).   lse: fp32
+ *            [total_q][n_heads] or NULL.
+ *   ws       ml4_workspace_bytes(ML4_ENTRY_MLA, ...) bytes (split-K partials; may be 0).
+ * Dequantisation of e4m3 codes is exact; QK and PV run on bf16 MFMA with fp32 accumulation.
+ */
+int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
+                          int32_t q_dtype, int32_t n_heads, int32_t rope_dim,
+                          const int32_t* topk_idx, const int32_t* topk_len, int32_t top_k,
+                          float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
+                          float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
+                          hipStream_t stream);
+
+/* One layer's role.  [blog, Model architecture (every 4th layer NoPE; 28 layers reuse the
+ * nearest preceding indexer layer's top-k; NoPE layers 39-71 read layer 35's latent KV);
+ * 跨层 KV 共享 (kv_sharing_target_layer_name); 稀疏 MLA + DSA indexer (shared indexer layers
+ * reuse the top-k)] */
+typedef struct {
+  int32_t layer;                    /* this layer's index, < n_layers                       */
+  int32_t kv_sharing_target_layer;  /* -1: own latent cache; else an earlier layer whose
+                                       cache this consumer reads (no write)                 */
+  int32_t topk_source_layer;        /* -1: run own indexer; else an earlier indexer layer
+                                       whose top-k is reused bit for bit                    */
+  int32_t rope_dim;                 /* 64, or 0 for NoPE                                     */
+  int32_t top_k;                    /* index_topk, 1 .. 2048                                 */
+  int32_t idx_heads;                /* indexer heads (multiple of 16, 16 .. 64)              */
+  int32_t mla_heads;                /* MLA heads (multiple of 16, 16 .. 128)                 */
+  float softmax_scale;              /* e.g. 1/sqrt(512 + rope_dim)                           */
+  float ssmax_s;                    /* MLA SSMax s (<= 0: off)                               */
+  float idx_ssmax_s;                /* indexer SSMax s (<= 0: off)                           */
+} ml4_layer;
+
+/*
+ * ml4_sparse_attn_layer -- one layer's indexer -> top-k -> sparse MLA in one call, no host
+ * synchronisation.  [blog, ROCm implementation details › 专用解码 (the whole indexer, exact
+ * top-2048 and sparse MLA inside one launch per layer, with NoPE, KV-sharing and
+ * index-sharing layers)]
+ *   lat_caches, idx_caches: [host] arrays of n_layers caches, indexed by layer.
+ *   topk_bufs, topk_lens: [host] arrays of n_layers device pointers, indexed by layer.
+ *   An indexer layer (topk_source_layer < 0) scores idx_caches[layer], selects, and writes
+ *   topk_bufs[layer] / topk_lens[layer]; a shared-indexer layer reads
+ *   topk_bufs[topk_source_layer] and runs no indexer.  The attention reads
+ *   lat_caches[kv_sharing_target_layer >= 0 ? kv_sharing_target_layer : layer].
+ *   q_idx/q_idx_scale/w_idx as in ml4_indexer_score (ignored for a shared-indexer layer);
+ *   q_mla/out/lse as in ml4_sparse_mla_decode.
+ *   ws: ml4_workspace_bytes(ML4_ENTRY_LAYER, s, mla_heads, top_k) bytes (holds the scores).
+ */
+int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache* lat_caches,
+                          const ml4_cache* idx_caches, int32_t n_layers, const void* q_idx,
+                          int32_t q_idx_dtype, const float* q_idx_scale, const float* w_idx,
+                          const void* q_mla, int32_t q_mla_dtype, int32_t* const* topk_bufs,
+                          int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
+                          void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream);
+
+enum ml4_entry { ML4_ENTRY_TOPK = 1, ML4_ENTRY_MLA = 2, ML4_ENTRY_LAYER = 3 };
+
+/* Workspace bytes an entry point needs for this batch (256-B aligned start required).
+ * n_heads = MLA heads; top_k as passed to the entry.  [host] s. */
+size_t ml4_workspace_bytes(int32_t entry, const ml4_seqs* s, int32_t n_heads, int32_t top_k);
+
+/* Thread-local text of the last failure: one line per failed check.  Never NULL. */
+const char* ml4_last_error(void);
+
+/* Copies the fault word to *bits [host] after synchronising `stream`; returns ML4_OK when
+ * no bit is set, ML4_E_DEVICE_FAULT otherwise.  The only synchronising call. */
+int ml4_fault_query(const uint32_t* fault, uint32_t* bits, hipStream_t stream);
+
+/* ML4_ABI_VERSION of the loaded library. */
+int ml4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ML4DSA_H */

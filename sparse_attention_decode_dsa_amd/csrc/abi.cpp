@@ -1,0 +1,392 @@
+// C-ABI shim: default-deny argument validation, workspace carving and kernel dispatch.
+//
+// Every check of an entry point is evaluated; each failure adds one line to the
+// thread-local error text and nothing is launched [page "vLLM 首日支持 Mistral Large 4"
+// (best2ai.com), ROCm implementation details › 专用解码: the path refuses unsupported
+// deployments at start-up with an error that lists every reason].
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "ml4_launch.h"
+#include "ml4dsa.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Checks {
+  std::vector<std::string> invalid, unsupported, workspace;
+  void bad(bool cond, const char* what) { if (cond) invalid.emplace_back(what); }
+  void unsup(bool cond, const char* what) { if (cond) unsupported.emplace_back(what); }
+  void ws(bool cond, const std::string& what) { if (cond) workspace.push_back(what); }
+  int finish(const char* entry) {
+    std::string msg;
+    auto add = [&](const std::vector<std::string>& v, const char* kind) {
+      for (const auto& m : v) msg += std::string(entry) + ": " + kind + ": " + m + "\n";
+    };
+    add(invalid, "invalid");
+    add(unsupported, "unsupported");
+    add(workspace, "workspace");
+    g_last_error = msg;
+    if (!invalid.empty()) return ML4_E_INVALID;
+    if (!unsupported.empty()) return ML4_E_UNSUPPORTED;
+    if (!workspace.empty()) return ML4_E_WORKSPACE;
+    return ML4_OK;
+  }
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int v) { int l = 0; while ((1 << l) < v) ++l; return l; }
+
+constexpr int kMaxSeqLen = 1 << 24;
+
+void check_seqs(Checks& c, const ml4_seqs* s) {
+  c.bad(s == nullptr, "seqs is NULL");
+  if (!s) return;
+  c.bad(s->batch < 1, "seqs.batch must be >= 1");
+  c.bad(s->total_q < 1, "seqs.total_q must be >= 1");
+  c.bad(s->max_seq_len < 1, "seqs.max_seq_len must be >= 1");
+  c.unsup(s->max_seq_len > kMaxSeqLen, "seqs.max_seq_len above 16,777,216");
+  c.bad(s->max_q_per_seq < 1, "seqs.max_q_per_seq must be >= 1");
+  c.bad(s->max_q_per_seq > s->total_q, "seqs.max_q_per_seq exceeds total_q");
+  c.bad(!pow2(s->block_size), "seqs.block_size must be a power of two");
+  c.unsup(pow2(s->block_size) && (s->block_size < 16 || s->block_size > 65536),
+          "seqs.block_size outside 16 .. 65536");
+  if (pow2(s->block_size) && s->max_seq_len >= 1)
+    c.bad((int64_t)s->max_blocks_per_seq * s->block_size < s->max_seq_len,
+          "seqs.max_blocks_per_seq * block_size < max_seq_len");
+  c.bad(!s->seq_lens || !s->q_start || !s->q_pos || !s->block_table,
+        "seqs arrays (seq_lens, q_start, q_pos, block_table) must be non-NULL");
+  c.bad(!aligned(s->seq_lens, 4) || !aligned(s->q_start, 4) || !aligned(s->q_pos, 4) ||
+            !aligned(s->block_table, 4),
+        "seqs arrays must be 4-byte aligned");
+}
+
+ml4::SeqView view(const ml4_seqs* s) {
+  ml4::SeqView v{};
+  v.batch = s->batch;
+  v.total_q = s->total_q;
+  v.max_seq_len = s->max_seq_len;
+  v.max_q_per_seq = s->max_q_per_seq;
+  v.lbs = ilog2(s->block_size);
+  v.mbps = s->max_blocks_per_seq;
+  v.seq_lens = s->seq_lens;
+  v.q_start = s->q_start;
+  v.q_pos = s->q_pos;
+  v.block_table = s->block_table;
+  return v;
+}
+
+void check_cache(Checks& c, const ml4_cache* k, bool index, const char* name) {
+  std::string n(name);
+  if (!k) { c.invalid.push_back(n + " is NULL"); return; }
+  if (!k->pool) c.invalid.push_back(n + ".pool is NULL");
+  if (!aligned(k->pool, 16)) c.invalid.push_back(n + ".pool must be 16-byte aligned");
+  if (k->num_blocks < 1) c.invalid.push_back(n + ".num_blocks must be >= 1");
+  if (index && k->format != ML4_IDX_F32 && k->format != ML4_IDX_FP8_132)
+    c.invalid.push_back(n + ".format is not an ml4_index_format");
+  if (!index && k->format != ML4_LAT_F32 && k->format != ML4_LAT_FP8_656)
+    c.invalid.push_back(n + ".format is not an ml4_latent_format");
+}
+
+std::string bytes_msg(const char* what, size_t need, size_t have) {
+  char buf[160];
+  snprintf(buf, sizeof buf, "%s needs %zu bytes, %zu given", what, need, have);
+  return buf;
+}
+
+int launch_status(hipError_t e, const char* entry) {
+  if (e == hipSuccess) return ML4_OK;
+  g_last_error = std::string(entry) + ": launch: " + hipGetErrorString(e) + "\n";
+  return ML4_E_LAUNCH;
+}
+
+size_t layer_scores_bytes(const ml4_seqs* s) {
+  const size_t ld = ml4::align_up((size_t)s->max_seq_len, 4);
+  return ml4::align_up((size_t)s->total_q * ld * sizeof(float), 256);
+}
+
+// ---- per-entry validation (shared by the fused entry) ----
+void check_scores(Checks& c, const ml4_seqs* s, const float* scores, int64_t ld) {
+  c.bad(!scores, "scores is NULL");
+  c.bad(!aligned(scores, 16), "scores must be 16-byte aligned");
+  if (s) c.bad(ld < s->max_seq_len, "ld_scores < max_seq_len");
+  c.bad(ld % 4 != 0, "ld_scores must be a multiple of 4");
+}
+
+void check_indexer(Checks& c, const ml4_cache* ic, const void* q, int32_t q_dtype,
+                   const float* w, int32_t n_heads, float ssmax_s) {
+  check_cache(c, ic, true, "idx_cache");
+  c.bad(!q, "q is NULL");
+  c.bad(!aligned(q, 16), "q must be 16-byte aligned");
+  c.bad(!w, "w is NULL");
+  if (ic) {
+    c.bad(ic->format == ML4_IDX_FP8_132 && q_dtype != ML4_FP8_E4M3,
+          "an ML4_IDX_FP8_132 cache needs ML4_FP8_E4M3 queries");
+    c.bad(ic->format == ML4_IDX_F32 && q_dtype != ML4_F32,
+          "an ML4_IDX_F32 cache needs ML4_F32 queries");
+  }
+  c.unsup(n_heads < 16 || n_heads > 64 || n_heads % 16 != 0,
+          "n_heads must be a multiple of 16 in 16 .. 64");
+  c.bad(!std::isfinite(ssmax_s), "ssmax_s must be finite");
+}
+
+void check_topk(Checks& c, int32_t top_k, const int32_t* idx, const int32_t* len) {
+  c.bad(top_k < 1, "top_k must be >= 1");
+  c.unsup(top_k > ML4_MAX_TOPK, "top_k above 2048");
+  c.bad(!idx || !len, "topk_idx and topk_len must be non-NULL");
+}
+
+void check_mla(Checks& c, const ml4_cache* kv, const void* q, int32_t q_dtype, int32_t n_heads,
+               int32_t rope_dim, const int32_t* idx, const int32_t* len, int32_t top_k,
+               float softmax_scale, float ssmax_s, const void* out, int32_t out_dtype) {
+  check_cache(c, kv, false, "kv");
+  c.bad(!q, "q is NULL");
+  c.bad(!aligned(q, 16), "q must be 16-byte aligned");
+  if (kv) {
+    c.bad(kv->format == ML4_LAT_FP8_656 && q_dtype != ML4_BF16,
+          "an ML4_LAT_FP8_656 cache needs ML4_BF16 queries");
+    c.bad(kv->format == ML4_LAT_FP8_656 && out_dtype != ML4_BF16,
+          "an ML4_LAT_FP8_656 cache writes ML4_BF16 outputs");
+    c.bad(kv->format == ML4_LAT_F32 && (q_dtype != ML4_F32 || out_dtype != ML4_F32),
+          "an ML4_LAT_F32 cache needs ML4_F32 queries and outputs");
+  }
+  c.unsup(n_heads < 16 || n_heads > 128 || n_heads % 16 != 0,
+          "n_heads must be a multiple of 16 in 16 .. 128");
+  c.unsup(rope_dim != 0 && rope_dim != ML4_ROPE_DIM, "rope_dim must be 64 or 0 (NoPE)");
+  c.bad(!idx || !len, "topk_idx and topk_len must be non-NULL");
+  c.bad(top_k < 1, "top_k must be >= 1");
+  c.unsup(top_k > ML4_MAX_TOPK, "top_k above 2048");
+  c.bad(!(softmax_scale > 0.f) || !std::isfinite(softmax_scale),
+        "softmax_scale must be finite and > 0");
+  c.bad(!std::isfinite(ssmax_s), "ssmax_s must be finite");
+  c.bad(!out, "out is NULL");
+  c.bad(!aligned(out, 16), "out must be 16-byte aligned");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ml4_abi_version(void) { return ML4_ABI_VERSION; }
+
+const char* ml4_last_error(void) { return g_last_error.c_str(); }
+
+size_t ml4_workspace_bytes(int32_t entry, const ml4_seqs* s, int32_t n_heads, int32_t top_k) {
+  if (!s || s->total_q < 1 || s->max_seq_len < 1 || !pow2(s->block_size)) return 0;
+  const ml4::SeqView v = view(s);
+  const size_t tk = ml4::align_up(ml4::topk_ws_bytes(v, top_k), 256);
+  const size_t ml = ml4::align_up(ml4::mla_ws_bytes(v, n_heads, top_k), 256);
+  switch (entry) {
+    case ML4_ENTRY_TOPK: return tk;
+    case ML4_ENTRY_MLA: return ml;
+    case ML4_ENTRY_LAYER: return layer_scores_bytes(s) + tk + ml;
+    default: return 0;
+  }
+}
+
+int ml4_indexer_score(const ml4_seqs* s, const ml4_cache* idx_cache, const void* q,
+                      int32_t q_dtype, const float* q_scale, const float* w, int32_t n_heads,
+                      float ssmax_s, float* scores, int64_t ld_scores, uint32_t* fault,
+                      hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  check_indexer(c, idx_cache, q, q_dtype, w, n_heads, ssmax_s);
+  check_scores(c, s, scores, ld_scores);
+  if (int rc = c.finish("ml4_indexer_score")) return rc;
+  ml4::IndexerLaunch a{};
+  a.s = view(s);
+  a.pool = idx_cache->pool;
+  a.num_blocks = idx_cache->num_blocks;
+  a.fp8 = idx_cache->format == ML4_IDX_FP8_132;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.n_heads = n_heads;
+  a.ssmax_s = ssmax_s;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.fault = fault;
+  return launch_status(ml4::launch_indexer(a, stream), "ml4_indexer_score");
+}
+
+int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, int32_t top_k,
+                    int32_t* topk_idx, int32_t* topk_len, void* ws, size_t ws_bytes,
+                    uint32_t* fault, hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  check_scores(c, s, scores, ld_scores);
+  check_topk(c, top_k, topk_idx, topk_len);
+  if (c.invalid.empty() && c.unsupported.empty()) {
+    const size_t need = ml4_workspace_bytes(ML4_ENTRY_TOPK, s, 0, top_k);
+    c.ws(ws_bytes < need, bytes_msg("top-k workspace", need, ws_bytes));
+    c.ws(need && (!ws || !aligned(ws, 256)), "workspace must be non-NULL and 256-byte aligned");
+  }
+  if (int rc = c.finish("ml4_topk_select")) return rc;
+  ml4::TopkLaunch a{};
+  a.s = view(s);
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.top_k = top_k;
+  a.idx = topk_idx;
+  a.len = topk_len;
+  a.ws = ws;
+  a.fault = fault;
+  return launch_status(ml4::launch_topk(a, stream), "ml4_topk_select");
+}
+
+int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
+                          int32_t q_dtype, int32_t n_heads, int32_t rope_dim,
+                          const int32_t* topk_idx, const int32_t* topk_len, int32_t top_k,
+                          float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
+                          float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
+                          hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  check_mla(c, kv, q, q_dtype, n_heads, rope_dim, topk_idx, topk_len, top_k, softmax_scale,
+            ssmax_s, out, out_dtype);
+  if (c.invalid.empty() && c.unsupported.empty()) {
+    const size_t need = ml4_workspace_bytes(ML4_ENTRY_MLA, s, n_heads, top_k);
+    c.ws(ws_bytes < need, bytes_msg("sparse-MLA workspace", need, ws_bytes));
+    c.ws(need && (!ws || !aligned(ws, 256)), "workspace must be non-NULL and 256-byte aligned");
+  }
+  if (int rc = c.finish("ml4_sparse_mla_decode")) return rc;
+  ml4::MlaLaunch a{};
+  a.s = view(s);
+  a.pool = kv->pool;
+  a.num_blocks = kv->num_blocks;
+  a.fp8 = kv->format == ML4_LAT_FP8_656;
+  a.q = q;
+  a.n_heads = n_heads;
+  a.rope_dim = rope_dim;
+  a.idx = topk_idx;
+  a.len = topk_len;
+  a.top_k = top_k;
+  a.softmax_scale = softmax_scale;
+  a.ssmax_s = ssmax_s;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.fault = fault;
+  return launch_status(ml4::launch_mla(a, stream), "ml4_sparse_mla_decode");
+}
+
+int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache* lat_caches,
+                          const ml4_cache* idx_caches, int32_t n_layers, const void* q_idx,
+                          int32_t q_idx_dtype, const float* q_idx_scale, const float* w_idx,
+                          const void* q_mla, int32_t q_mla_dtype, int32_t* const* topk_bufs,
+                          int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
+                          void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  c.bad(L == nullptr, "layer descriptor is NULL");
+  c.bad(n_layers < 1, "n_layers must be >= 1");
+  c.bad(!lat_caches || !topk_bufs || !topk_lens, "lat_caches, topk_bufs, topk_lens must be non-NULL");
+  if (!L || n_layers < 1 || !lat_caches || !topk_bufs || !topk_lens) return c.finish("ml4_sparse_attn_layer");
+  const int l = L->layer;
+  c.bad(l < 0 || l >= n_layers, "layer outside 0 .. n_layers-1");
+  const int tgt = L->kv_sharing_target_layer, src = L->topk_source_layer;
+  c.bad(tgt != -1 && (tgt < 0 || tgt >= l),
+        "kv_sharing_target_layer must be -1 or an earlier layer");
+  c.bad(src != -1 && (src < 0 || src >= l), "topk_source_layer must be -1 or an earlier layer");
+  if (l < 0 || l >= n_layers || (tgt != -1 && (tgt < 0 || tgt >= l)) ||
+      (src != -1 && (src < 0 || src >= l)))
+    return c.finish("ml4_sparse_attn_layer");
+  const int lat_layer = tgt >= 0 ? tgt : l;
+  const bool own_indexer = src < 0;
+  const int topk_layer = own_indexer ? l : src;
+  c.bad(!topk_bufs[topk_layer] || !topk_lens[topk_layer],
+        own_indexer ? "topk_bufs[layer] / topk_lens[layer] must be non-NULL"
+                    : "topk_bufs[topk_source_layer] / topk_lens[topk_source_layer] must be non-NULL");
+  const int64_t ld = s ? (int64_t)ml4::align_up((size_t)s->max_seq_len, 4) : 0;
+  float* scores = static_cast<float*>(ws);
+  if (own_indexer) {
+    c.bad(!idx_caches, "idx_caches is NULL for an indexer layer");
+    if (idx_caches)
+      check_indexer(c, &idx_caches[l], q_idx, q_idx_dtype, w_idx, L->idx_heads, L->idx_ssmax_s);
+    check_topk(c, L->top_k, topk_bufs[topk_layer], topk_lens[topk_layer]);
+  }
+  check_mla(c, &lat_caches[lat_layer], q_mla, q_mla_dtype, L->mla_heads, L->rope_dim,
+            topk_bufs[topk_layer], topk_lens[topk_layer], L->top_k, L->softmax_scale, L->ssmax_s,
+            out, out_dtype);
+  size_t need = 0;
+  if (c.invalid.empty() && c.unsupported.empty() && s) {
+    need = ml4_workspace_bytes(ML4_ENTRY_LAYER, s, L->mla_heads, L->top_k);
+    c.ws(ws_bytes < need, bytes_msg("layer workspace", need, ws_bytes));
+    c.ws(!ws || !aligned(ws, 256), "workspace must be non-NULL and 256-byte aligned");
+  }
+  if (int rc = c.finish("ml4_sparse_attn_layer")) return rc;
+
+  const ml4::SeqView v = view(s);
+  char* wsp = static_cast<char*>(ws);
+  const size_t sc_bytes = layer_scores_bytes(s);
+  const size_t tk_bytes = ml4::align_up(ml4::topk_ws_bytes(v, L->top_k), 256);
+  hipError_t e = hipSuccess;
+  if (own_indexer) {
+    ml4::IndexerLaunch ia{};
+    ia.s = v;
+    ia.pool = idx_caches[l].pool;
+    ia.num_blocks = idx_caches[l].num_blocks;
+    ia.fp8 = idx_caches[l].format == ML4_IDX_FP8_132;
+    ia.q = q_idx;
+    ia.q_scale = q_idx_scale;
+    ia.w = w_idx;
+    ia.n_heads = L->idx_heads;
+    ia.ssmax_s = L->idx_ssmax_s;
+    ia.scores = scores;
+    ia.ld = ld;
+    ia.fault = fault;
+    e = ml4::launch_indexer(ia, stream);
+    if (e != hipSuccess) return launch_status(e, "ml4_sparse_attn_layer");
+    ml4::TopkLaunch ta{};
+    ta.s = v;
+    ta.scores = scores;
+    ta.ld = ld;
+    ta.top_k = L->top_k;
+    ta.idx = topk_bufs[l];
+    ta.len = topk_lens[l];
+    ta.ws = wsp + sc_bytes;
+    ta.fault = fault;
+    e = ml4::launch_topk(ta, stream);
+    if (e != hipSuccess) return launch_status(e, "ml4_sparse_attn_layer");
+  }
+  ml4::MlaLaunch ma{};
+  ma.s = v;
+  ma.pool = lat_caches[lat_layer].pool;
+  ma.num_blocks = lat_caches[lat_layer].num_blocks;
+  ma.fp8 = lat_caches[lat_layer].format == ML4_LAT_FP8_656;
+  ma.q = q_mla;
+  ma.n_heads = L->mla_heads;
+  ma.rope_dim = L->rope_dim;
+  ma.idx = topk_bufs[topk_layer];
+  ma.len = topk_lens[topk_layer];
+  ma.top_k = L->top_k;
+  ma.softmax_scale = L->softmax_scale;
+  ma.ssmax_s = L->ssmax_s;
+  ma.out = out;
+  ma.lse = lse;
+  ma.ws = wsp + sc_bytes + tk_bytes;
+  ma.fault = fault;
+  return launch_status(ml4::launch_mla(ma, stream), "ml4_sparse_attn_layer");
+}
+
+int ml4_fault_query(const uint32_t* fault, uint32_t* bits, hipStream_t stream) {
+  if (!fault || !bits) {
+    g_last_error = "ml4_fault_query: invalid: fault and bits must be non-NULL\n";
+    return ML4_E_INVALID;
+  }
+  uint32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, fault, sizeof h, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return launch_status(e, "ml4_fault_query");
+  *bits = h;
+  return h ? ML4_E_DEVICE_FAULT : ML4_OK;
+}
+
+}  // extern "C"

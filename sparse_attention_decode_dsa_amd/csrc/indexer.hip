@@ -1,0 +1,287 @@
+// DSA indexer scores on gfx950.
+//
+// Pages: "vLLM 首日支持 Mistral Large 4" (best2ai.com), Implementation details › 稀疏 MLA + DSA
+// indexer (FP8 indexer cache; the indexer has its own SSMax) and ROCm implementation details ›
+// AITER 上的 DSA 索引器 (132-byte FP8 keys with one scale per key; paged decode scores and
+// prefill scores read the FP8 keys).
+//
+//   s[r, t] = m_r * ks[t] * sum_h w[r,h] * qs[r,h] * ReLU(q[r,h,:] . k[t,:])
+//
+// The 64 x 128 x n product per query row is a real GEMM even for one decode token, so it
+// runs on the matrix cores: heads on the MFMA M axis (16 per tile), keys on N, the 128 key
+// dims on K.  It uses v_mfma_f32_16x16x32_f16: every e4m3 code converts exactly to fp16, so
+// products are exact and the four K=32 steps accumulate in fp32.  (The fp8 form
+// v_mfma_f32_16x16x128_f8f6f4 drops low-order bits of small products inside its 128-term sum
+// -- measured up to 1.3e-5 of sum |q_d k_d| on gfx950 against 6.5e-8 for the 16-bit forms --
+// which moves keys across the top-k boundary.)
+//
+// A work-group owns one request's run of up to 4 query rows and a chunk of its keys.  Key
+// rows stream from HBM in 64-key steps (8,448 contiguous bytes when a block holds >= 64
+// tokens): each thread loads 32 bytes of a row, decodes them to fp16 and writes them to a
+// double-buffered LDS tile, so a key is fetched and decoded once for all rows.  Each wave
+// owns one query row (its 64 x 128 query stays in registers) and 16-key sub-tiles of the
+// step; the weighted-ReLU head reduction runs in-lane over the 4 heads a lane holds per
+// tile, then across the 4 lane groups.
+#include "ml4_device.h"
+
+namespace ml4 {
+
+namespace {
+
+constexpr int kIdxRow = 132;
+constexpr int kStepKeys = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kKeyStride = 136;   // fp16 per key row in LDS (128 + 8): conflict-free b128 reads
+
+// R = query rows per work-group (1, 2 or 4), HT = 16-head tiles (n_heads / 16).
+template <int R, int HT>
+__global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int groups_per_seq,
+                                                          int keys_per_wg) {
+  __shared__ __attribute__((aligned(16))) _Float16 ktile[2][kStepKeys * kKeyStride];
+  __shared__ float kscale[2][kStepKeys];
+  __shared__ int kok[2][kStepKeys / 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int g16 = lane >> 4;
+  const int c16 = lane & 15;
+  const SeqView& s = a.s;
+  const int b = blockIdx.y / groups_per_seq;
+  const int grp = blockIdx.y - b * groups_per_seq;
+  const int q0 = s.q_start[b];
+  const int nq = s.q_start[b + 1] - q0;
+  const int row0 = q0 + grp * R;
+  const int nrows = min(R, nq - grp * R);
+  if (nrows <= 0) return;
+  const int seq_len = s.seq_lens[b];
+  const int k_lo = blockIdx.x * keys_per_wg;
+  const int k_hi = min(k_lo + keys_per_wg, s.max_seq_len);
+  if (k_lo >= k_hi) return;
+
+  // Positions of the work-group's rows; the keys it must score end at the largest.
+  int pmax = -1;
+  for (int j = 0; j < nrows; ++j) {
+    const int p = s.q_pos[row0 + j];
+    if (p >= 0 && p < seq_len && p < s.max_seq_len) pmax = max(pmax, p);
+  }
+  // This wave's row: wave % R (waves beyond nrows mirror row 0 but write nothing).
+  const int jr = wave % R;
+  const bool row_live = jr < nrows;
+  const int row = row0 + (row_live ? jr : 0);
+  int pos = s.q_pos[row];
+  if (pos < 0 || pos >= seq_len || pos >= s.max_seq_len) {
+    if (row_live && blockIdx.x == 0 && lane == 0) raise_fault(a.fault, 1u << 3);
+    pos = -1;
+  }
+  // The 4/R waves of a row split the step's four 16-key sub-tiles: wave / R, + 4 / R, ...
+  constexpr int kSubPerWave = R;
+  const int sub0 = wave / R;
+
+  // Query fragments (A operand: head on M, dims on K).  Lane group g holds dims 32g .. 32g+31
+  // as four K=32 chunks; the key side uses the same split, so the dims pair up.
+  f16x8 qa[HT][4];
+  float wq[HT][4];
+  const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint8_t* qp = qbase + ((size_t)row * a.n_heads + ht * 16 + c16) * 128 + 32 * g16;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(qp);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(qp + 16);
+    const uint32_t w8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x4 lo = e4m3x4_to_f16(w8[2 * c]);
+      const f16x4 hi = e4m3x4_to_f16(w8[2 * c + 1]);
+      qa[ht][c] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = (size_t)row * a.n_heads + ht * 16 + 4 * g16 + i;
+      wq[ht][i] = a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f);
+    }
+  }
+  const float mrow = ssmax_mult(a.ssmax_s, max(pos, 0));
+
+  const int32_t* bt = s.block_table + (size_t)b * s.mbps;
+  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
+  const int bs_mask = (1 << s.lbs) - 1;
+  const float ninf = -__builtin_inff();
+
+  // Staging: thread -> (key kk = tid / 4, quarter qq = tid % 4) of a 64-key step.
+  const int kk = tid >> 2, qq = tid & 3;
+  u32x4 st_lo, st_hi;
+  float st_scale;
+  int st_ok;
+  auto load_step = [&](int t0) {
+    st_lo = u32x4{0, 0, 0, 0};
+    st_hi = u32x4{0, 0, 0, 0};
+    st_scale = 0.f;
+    st_ok = 0;
+    const int t = t0 + kk;
+    if (t > pmax || t >= k_hi) return;      // past every row: no block of the table is read
+    const int blk = bt[t >> s.lbs];   // 16 consecutive keys share a block (bs >= 16)
+    if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
+      if (qq == 0 && (kk & 15) == 0) raise_fault(a.fault, 1u << 0);
+      return;
+    }
+    const uint8_t* rp = pool + (((int64_t)blk << s.lbs) + (t & bs_mask)) * kIdxRow;
+    const u32x4a4 v0 = *reinterpret_cast<const u32x4a4*>(rp + 32 * qq);
+    const u32x4a4 v1 = *reinterpret_cast<const u32x4a4*>(rp + 32 * qq + 16);
+    st_lo = u32x4{v0[0], v0[1], v0[2], v0[3]};
+    st_hi = u32x4{v1[0], v1[1], v1[2], v1[3]};
+    if (qq == 0) st_scale = *reinterpret_cast<const float*>(rp + 128);
+    st_ok = 1;
+  };
+  auto store_step = [&](int buf) {
+    _Float16* dst = &ktile[buf][kk * kKeyStride + 32 * qq];
+    const uint32_t w8[8] = {st_lo[0], st_lo[1], st_lo[2], st_lo[3],
+                            st_hi[0], st_hi[1], st_hi[2], st_hi[3]};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x4 lo = e4m3x4_to_f16(w8[2 * c]);
+      const f16x4 hi = e4m3x4_to_f16(w8[2 * c + 1]);
+      *reinterpret_cast<f16x8*>(dst + 8 * c) =
+          f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    if (qq == 0) kscale[buf][kk] = st_scale;
+    if (qq == 0 && (kk & 15) == 0) kok[buf][kk >> 4] = st_ok;
+  };
+
+  const int nsteps = (min(k_hi, pmax + 1) - k_lo + kStepKeys - 1) / kStepKeys;
+  // Keys past every row's position only get -inf.
+  for (int t = max(k_lo, pmax + 1) + tid; t < k_hi; t += kThreads)
+    for (int j = 0; j < nrows; ++j) a.scores[(size_t)(row0 + j) * a.ld + t] = ninf;
+  if (nsteps <= 0) return;
+
+  load_step(k_lo);
+  store_step(0);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int t0 = k_lo + st * kStepKeys;
+    const int buf = st & 1;
+    if (st + 1 < nsteps) load_step(t0 + kStepKeys);   // in flight during this step
+
+#pragma unroll
+    for (int si = 0; si < kSubPerWave; ++si) {
+      const int sub = sub0 + si * (kWaves / R);
+      const int tk = t0 + 16 * sub;
+      if (tk >= k_hi) continue;
+      const int t = tk + c16;
+      float part = 0.f;
+      const bool ok = kok[buf][sub] != 0;
+      if (ok) {
+        const _Float16* krow = &ktile[buf][(16 * sub + c16) * kKeyStride + 32 * g16];
+        f16x8 kb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const f16x8*>(krow + 8 * c);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          f32x4 d{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) d = mfma_f16(qa[ht][c], kb[c], d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part += wq[ht][i] * fmaxf(d[i], 0.f);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+      }
+      if (row_live && lane < 16 && t < k_hi)
+        a.scores[(size_t)row * a.ld + t] =
+            (ok && t <= pos) ? part * kscale[buf][16 * sub + c16] * mrow : ninf;
+    }
+    if (st + 1 < nsteps) {
+      store_step(buf ^ 1);   // the other buffer was last read two steps ago
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 format: 128 x fp32 per key, no key scale, fp32 queries.  One thread per key, the
+// row's queries in LDS.
+__global__ __launch_bounds__(256) void k_indexer_f32(IndexerLaunch a) {
+  __shared__ float qsh[64 * 128];
+  __shared__ float wsh[64];
+  const SeqView& s = a.s;
+  const int r = blockIdx.y;
+  const int b = request_of(s.q_start, s.batch, r);
+  const int H = a.n_heads;
+  const float* q = static_cast<const float*>(a.q) + (size_t)r * H * 128;
+  for (int i = threadIdx.x; i < H * 128; i += 256) qsh[i] = q[i];
+  for (int h = threadIdx.x; h < H; h += 256)
+    wsh[h] = a.w[(size_t)r * H + h] * (a.q_scale ? a.q_scale[(size_t)r * H + h] : 1.0f);
+  __syncthreads();
+  int p = s.q_pos[r];
+  if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) raise_fault(a.fault, 1u << 3);
+    p = -1;
+  }
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= s.max_seq_len) return;
+  float* out = a.scores + (size_t)r * a.ld + t;
+  if (t > p) {
+    *out = -__builtin_inff();
+    return;
+  }
+  const int blk = s.block_table[(size_t)b * s.mbps + (t >> s.lbs)];
+  if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
+    raise_fault(a.fault, 1u << 0);
+    *out = -__builtin_inff();
+    return;
+  }
+  const float* k = static_cast<const float*>(a.pool) +
+                   (((int64_t)blk << s.lbs) + (t & ((1 << s.lbs) - 1))) * 128;
+  float kr[128];
+#pragma unroll
+  for (int i = 0; i < 128; i += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(k + i);
+    kr[i] = v[0]; kr[i + 1] = v[1]; kr[i + 2] = v[2]; kr[i + 3] = v[3];
+  }
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 128; ++i) d = fmaf(qsh[h * 128 + i], kr[i], d);
+    acc += wsh[h] * fmaxf(d, 0.f);
+  }
+  *out = acc * ssmax_mult(a.ssmax_s, p);
+}
+
+template <int R>
+hipError_t dispatch_heads(const IndexerLaunch& a, dim3 grid, int gps, int kpw, hipStream_t st) {
+  switch (a.n_heads / 16) {
+    case 1: k_indexer_fp8<R, 1><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
+    case 2: k_indexer_fp8<R, 2><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
+    case 3: k_indexer_fp8<R, 3><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
+    case 4: k_indexer_fp8<R, 4><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
+  const SeqView& s = a.s;
+  if (!a.fp8) {
+    dim3 grid((s.max_seq_len + 255) / 256, s.total_q);
+    k_indexer_f32<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const int R = s.max_q_per_seq <= 1 ? 1 : (s.max_q_per_seq <= 2 ? 2 : 4);
+  const int gps = (s.max_q_per_seq + R - 1) / R;
+  const long long groups = (long long)s.batch * gps;
+  // Keys per work-group: long chunks amortise loading the queries; shrink them until the
+  // grid covers the 256 CUs several times over.
+  int kpw = 4096;
+  while (kpw > 256 && groups * ((s.max_seq_len + kpw - 1) / kpw) < 2048) kpw >>= 1;
+  dim3 grid((s.max_seq_len + kpw - 1) / kpw, (unsigned)groups);
+  switch (R) {
+    case 1: return dispatch_heads<1>(a, grid, gps, kpw, st);
+    case 2: return dispatch_heads<2>(a, grid, gps, kpw, st);
+    default: return dispatch_heads<4>(a, grid, gps, kpw, st);
+  }
+}
+
+}  // namespace ml4

@@ -1,0 +1,73 @@
+// Internal interface between the C-ABI shim (abi.cpp) and the kernel launchers.  Host-only
+// types; every pointer is a device pointer.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ml4 {
+
+struct SeqView {
+  int batch, total_q, max_seq_len, max_q_per_seq;
+  int lbs;    // log2(block_size)
+  int mbps;   // block_table row stride
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+};
+
+struct IndexerLaunch {
+  SeqView s;
+  const void* pool;
+  int64_t num_blocks;
+  bool fp8;             // ML4_IDX_FP8_132 + e4m3 q; else ML4_IDX_F32 + fp32 q
+  const void* q;
+  const float* q_scale; // may be null
+  const float* w;
+  int n_heads;
+  float ssmax_s;
+  float* scores;
+  int64_t ld;
+  uint32_t* fault;
+};
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
+
+struct TopkLaunch {
+  SeqView s;
+  const float* scores;
+  int64_t ld;
+  int top_k;
+  int32_t* idx;
+  int32_t* len;
+  void* ws;
+  uint32_t* fault;
+};
+size_t topk_ws_bytes(const SeqView& s, int top_k);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t st);
+
+struct MlaLaunch {
+  SeqView s;
+  const void* pool;
+  int64_t num_blocks;
+  bool fp8;             // ML4_LAT_FP8_656 + bf16 q/out; else ML4_LAT_F32 + fp32 q/out
+  const void* q;
+  int n_heads;
+  int rope_dim;
+  const int32_t* idx;
+  const int32_t* len;
+  int top_k;
+  float softmax_scale;
+  float ssmax_s;
+  void* out;
+  float* lse;           // may be null
+  void* ws;
+  uint32_t* fault;
+};
+size_t mla_ws_bytes(const SeqView& s, int n_heads, int top_k);
+hipError_t launch_mla(const MlaLaunch& a, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace ml4

@@ -1,0 +1,485 @@
+// Exact top-k per query row on gfx950.
+//
+// Pages: "vLLM 首日支持 Mistral Large 4" (best2ai.com), ROCm implementation details › 专用解码
+// (the persistent decode kernel computes an exact top-2048) and Long context › DCP (a stable
+// top-k merge; radix select over packed (score, id) candidates; top-k compaction: padded -1
+// slots bounded by topk_length).
+//
+// Selection is integer work on the order-preserving u32 image of each fp32 score (-0 folded
+// onto +0, NaN mapped below -inf), so it is exact and deterministic:
+//   1. AND/OR reduction of the keys: the leading bits common to every candidate are skipped.
+//   2. Radix passes of up to 11 bits below that prefix: an LDS histogram, a block-wide
+//      suffix scan to find the digit holding the k-th key, until the k-th key's bits are all
+//      known (or its bucket is taken whole).
+//   3. Ordered compaction in ascending t: keys above the threshold are kept; keys equal to it
+//      are kept lowest-t first until k are chosen (wave ballots + block prefix sums).
+// Rows up to 32,768 keys cache their keys in LDS after the first read; longer rows stream
+// from L2.  Rows longer than 131,072 keys use a multi-work-group version with the same
+// steps, one launch per step, its histograms merged with integer atomics.
+#include "ml4_device.h"
+
+namespace ml4 {
+
+namespace {
+
+constexpr int kRowThreads = 1024;
+constexpr int kCacheKeys = 32768;
+constexpr int kBigChunk = 4096;
+constexpr int kBigThreads = 256;
+constexpr int kMaxDigitBits = 11;
+constexpr uint32_t kFaultNan = 1u << 2;
+constexpr uint32_t kFaultQpos = 1u << 3;
+
+__device__ __forceinline__ uint32_t order_key(float f, bool& is_nan) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    is_nan = true;
+    return 0u;
+  }
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t digit_prefix(uint32_t key, int shift) {
+  return (uint64_t)key >> shift;   // shift in [0, 32]
+}
+
+// Exclusive prefix sum over the block; *total receives the block sum.  Every thread of the
+// block must call it.  sh needs NT/64 ints.
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* total, int* sh) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) sh[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < NW ? sh[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < NW; d <<= 1) {
+      const int y = __shfl_up(t, d);
+      if (lane >= d) t += y;
+    }
+    if (lane < NW) sh[lane] = t;
+  }
+  __syncthreads();
+  const int off = wave ? sh[wave - 1] : 0;
+  *total = sh[NW - 1];
+  __syncthreads();
+  return off + x - v;
+}
+
+// Given a histogram (nb bins, descending order of digit = descending key), find the digit d
+// with above(d) < need <= above(d) + hist[d].  Writes {d, above(d), hist[d]} to out.
+template <int NT>
+__device__ void find_digit(const uint32_t* hist, int nb, int need, int* out, int* sh) {
+  const int i0 = 2 * threadIdx.x;
+  const int d1 = nb - 1 - i0, d0 = nb - 2 - i0;
+  const int c1 = d1 >= 0 ? (int)hist[d1] : 0;
+  const int c0 = d0 >= 0 ? (int)hist[d0] : 0;
+  int total;
+  const int ex = block_exclusive_scan<NT>(c1 + c0, &total, sh);
+  if (d1 >= 0 && ex < need && need <= ex + c1) {
+    out[0] = d1; out[1] = ex; out[2] = c1;
+  } else if (d0 >= 0 && ex + c1 < need && need <= ex + c1 + c0) {
+    out[0] = d0; out[1] = ex + c1; out[2] = c0;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_out) {
+  const SeqView& s = a.s;
+  const int b = request_of(s.q_start, s.batch, r);
+  const int p = s.q_pos[r];
+  int32_t* out = a.idx + (size_t)r * a.top_k;
+  if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len || (int64_t)p >= a.ld) {
+    for (int i = threadIdx.x; i < a.top_k; i += blockDim.x) out[i] = -1;
+    if (threadIdx.x == 0) {
+      a.len[r] = 0;
+      raise_fault(a.fault, kFaultQpos);
+    }
+    return false;
+  }
+  const int n = p + 1;
+  if (n <= a.top_k) {
+    for (int i = threadIdx.x; i < a.top_k; i += blockDim.x) out[i] = i < n ? i : -1;
+    if (threadIdx.x == 0) a.len[r] = n;
+    return false;
+  }
+  *n_out = n;
+  return true;
+}
+
+// ------------------------------------------------------------------ one work-group per row
+template <bool CACHE>
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
+  extern __shared__ uint32_t kcache[];
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ int sh_scan[kRowThreads / kWave];
+  __shared__ uint32_t sh_and[kRowThreads / kWave], sh_or[kRowThreads / kWave];
+  __shared__ int sh_sel[4];
+  __shared__ int sh_nan;
+
+  const int r = blockIdx.x;
+  int n = 0;
+  if (!row_prologue(a, r, &n)) return;
+  const int K = a.top_k;
+  const float* row = a.scores + (size_t)r * a.ld;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+
+  auto key_at = [&](int t) -> uint32_t {
+    if (CACHE) return kcache[t];
+    bool nn = false;
+    return order_key(row[t], nn);
+  };
+
+  // 1. common leading bits of every candidate key
+  uint32_t av = ~0u, ov = 0u;
+  bool any_nan = false;
+  for (int t = tid; t < n; t += kRowThreads) {
+    bool nn = false;
+    const uint32_t k = order_key(row[t], nn);
+    any_nan |= nn;
+    av &= k;
+    ov |= k;
+    if (CACHE) kcache[t] = k;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    av &= (uint32_t)__shfl_xor((int)av, m);
+    ov |= (uint32_t)__shfl_xor((int)ov, m);
+  }
+  if (tid == 0) sh_nan = 0;
+  if (lane == 0) { sh_and[wave] = av; sh_or[wave] = ov; }
+  __syncthreads();
+  if (any_nan) sh_nan = 1;
+  av = ~0u; ov = 0u;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / kWave; ++w) { av &= sh_and[w]; ov |= sh_or[w]; }
+  __syncthreads();
+  if (tid == 0 && sh_nan) raise_fault(a.fault, kFaultNan);
+
+  const uint32_t diff = av ^ ov;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are common
+  uint64_t P = digit_prefix(av, shift);
+  int need = K;
+
+  // 2. radix passes below the common prefix
+  while (shift > 0) {
+    const int w = min(kMaxDigitBits, shift);
+    const int nsh = shift - w;
+    const int nb = 1 << w;
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int t = tid; t < n; t += kRowThreads) {
+      const uint32_t k = key_at(t);
+      if (digit_prefix(k, shift) == P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    const int d = sh_sel[0], above = sh_sel[1], cnt = sh_sel[2];
+    __syncthreads();
+    P = (P << w) | (uint64_t)d;
+    need -= above;
+    shift = nsh;
+    if (cnt == need) break;   // the whole bucket is selected
+  }
+
+  // 3. ordered compaction
+  int32_t* out = a.idx + (size_t)r * K;
+  int carry_eq = 0, carry_out = 0;
+  for (int base = 0; base < n && carry_out < K; base += kRowThreads) {
+    const int t = base + tid;
+    bool gt = false, eq = false;
+    if (t < n) {
+      const uint64_t h = digit_prefix(key_at(t), shift);
+      gt = h > P;
+      eq = h == P;
+    }
+    int tot_eq, tot_sel;
+    const int eq_rank = carry_eq + block_exclusive_scan<kRowThreads>(eq ? 1 : 0, &tot_eq, sh_scan);
+    const bool sel = gt || (eq && eq_rank < need);
+    const int at = carry_out + block_exclusive_scan<kRowThreads>(sel ? 1 : 0, &tot_sel, sh_scan);
+    if (sel && at < K) out[at] = t;
+    carry_eq += tot_eq;
+    carry_out += tot_sel;
+  }
+  if (tid == 0) a.len[r] = K;
+}
+
+// ------------------------------------------------------------------ many work-groups per row
+// Per-row selection state of the multi-work-group path.  The rule being refined is
+// "keep key if key >> shift > P; keep it if key >> shift == P and it is among the first
+// `need` such keys in t order"; `resolved` stops refinement once a bucket is taken whole.
+struct alignas(16) BigState {
+  uint32_t and_v, or_v, nan, active;
+  uint64_t P;
+  int shift, need;
+  int resolved, pad0, pad1, pad2;
+};
+
+struct BigWs {
+  BigState* st;    // [rows]
+  uint32_t* hist;  // [rows][2048]
+  int* cnt;        // [rows][chunks][2]  gt, eq  -> exclusive offsets after the scan
+  int chunks;
+};
+
+__host__ __device__ __forceinline__ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__device__ __forceinline__ BigWs big_ws(void* ws, int rows, int chunks) {
+  BigWs w;
+  char* p = static_cast<char*>(ws);
+  w.st = reinterpret_cast<BigState*>(p);
+  p += round256((size_t)rows * sizeof(BigState));
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += round256((size_t)rows * (1 << kMaxDigitBits) * 4);
+  w.cnt = reinterpret_cast<int*>(p);
+  w.chunks = chunks;
+  return w;
+}
+
+__global__ __launch_bounds__(kBigThreads) void k_tkb_init(TopkLaunch a, int chunks) {
+  const int r = blockIdx.x;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  for (int i = threadIdx.x; i < (1 << kMaxDigitBits); i += kBigThreads)
+    w.hist[(size_t)r * (1 << kMaxDigitBits) + i] = 0u;
+  int n = 0;
+  const bool active = row_prologue(a, r, &n);
+  if (threadIdx.x == 0) {
+    BigState s{~0u, 0u, 0u, active ? 1u : 0u, 0ull, 0, 0, 0, 0, 0, 0};
+    w.st[r] = s;
+  }
+}
+
+__global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chunks) {
+  const int r = blockIdx.y;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  if (!w.st[r].active) return;
+  const int n = a.s.q_pos[r] + 1;
+  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
+  if (lo >= hi) return;
+  const float* row = a.scores + (size_t)r * a.ld;
+  uint32_t av = ~0u, ov = 0u;
+  bool any_nan = false;
+  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
+    bool nn = false;
+    const uint32_t k = order_key(row[t], nn);
+    any_nan |= nn;
+    av &= k;
+    ov |= k;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    av &= (uint32_t)__shfl_xor((int)av, m);
+    ov |= (uint32_t)__shfl_xor((int)ov, m);
+  }
+  const bool wave_nan = __any(any_nan);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    atomicAnd(&w.st[r].and_v, av);
+    atomicOr(&w.st[r].or_v, ov);
+    if (wave_nan) atomicOr(&w.st[r].nan, 1u);
+  }
+}
+
+__global__ void k_tkb_setup(TopkLaunch a, int chunks) {
+  const int r = blockIdx.x;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  if (threadIdx.x != 0 || !w.st[r].active) return;
+  BigState& s = w.st[r];
+  if (s.nan) raise_fault(a.fault, kFaultNan);
+  const uint32_t diff = s.and_v ^ s.or_v;
+  s.shift = diff ? 32 - __builtin_clz(diff) : 0;
+  s.P = digit_prefix(s.and_v, s.shift);
+  s.need = a.top_k;
+}
+
+__global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chunks) {
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  const int r = blockIdx.y;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  const BigState s = w.st[r];
+  if (!s.active || s.shift == 0 || s.resolved) return;
+  const int n = a.s.q_pos[r] + 1;
+  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
+  if (lo >= hi) return;
+  const int wd = min(kMaxDigitBits, s.shift), nsh = s.shift - wd, nb = 1 << wd;
+  for (int i = threadIdx.x; i < nb; i += kBigThreads) hist[i] = 0u;
+  __syncthreads();
+  const float* row = a.scores + (size_t)r * a.ld;
+  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
+    bool nn = false;
+    const uint32_t k = order_key(row[t], nn);
+    if (digit_prefix(k, s.shift) == s.P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = w.hist + (size_t)r * (1 << kMaxDigitBits);
+  for (int i = threadIdx.x; i < nb; i += kBigThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_tkb_pick(TopkLaunch a, int chunks) {
+  __shared__ int sh_scan[kRowThreads / kWave];
+  __shared__ int sh_sel[4];
+  const int r = blockIdx.x;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  const BigState s = w.st[r];
+  if (!s.active || s.shift == 0 || s.resolved) return;
+  const int wd = min(kMaxDigitBits, s.shift), nb = 1 << wd;
+  uint32_t* g = w.hist + (size_t)r * (1 << kMaxDigitBits);
+  find_digit<kRowThreads>(g, nb, s.need, sh_sel, sh_scan);
+  const int d = sh_sel[0], above = sh_sel[1], cnt = sh_sel[2];
+  for (int i = threadIdx.x; i < nb; i += kRowThreads) g[i] = 0u;
+  if (threadIdx.x == 0) {
+    BigState& o = w.st[r];
+    o.P = (s.P << wd) | (uint64_t)d;
+    o.need = s.need - above;
+    o.shift = s.shift - wd;
+    o.resolved = (cnt == o.need) ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chunks) {
+  __shared__ int sh_gt[kBigThreads / kWave], sh_eq[kBigThreads / kWave];
+  const int r = blockIdx.y;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  const BigState s = w.st[r];
+  if (!s.active) return;
+  const int shift = s.shift;
+  const uint64_t P = s.P;
+  const int n = a.s.q_pos[r] + 1;
+  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
+  const float* row = a.scores + (size_t)r * a.ld;
+  int gt = 0, eq = 0;
+  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
+    bool nn = false;
+    const uint64_t h = digit_prefix(order_key(row[t], nn), shift);
+    gt += h > P;
+    eq += h == P;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) { gt += __shfl_xor(gt, m); eq += __shfl_xor(eq, m); }
+  if ((threadIdx.x & (kWave - 1)) == 0) { sh_gt[threadIdx.x >> 6] = gt; sh_eq[threadIdx.x >> 6] = eq; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int G = 0, E = 0;
+    for (int i = 0; i < kBigThreads / kWave; ++i) { G += sh_gt[i]; E += sh_eq[i]; }
+    int* c = w.cnt + ((size_t)r * chunks + blockIdx.x) * 2;
+    c[0] = G;
+    c[1] = E;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_tkb_scan(TopkLaunch a, int chunks) {
+  __shared__ int sh_scan[kRowThreads / kWave];
+  const int r = blockIdx.x;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  if (!w.st[r].active) return;
+  int* c = w.cnt + (size_t)r * chunks * 2;
+  int carry_gt = 0, carry_eq = 0;
+  for (int base = 0; base < chunks; base += kRowThreads) {
+    const int i = base + threadIdx.x;
+    const int g = i < chunks ? c[2 * i] : 0;
+    const int e = i < chunks ? c[2 * i + 1] : 0;
+    int tg, te;
+    const int xg = block_exclusive_scan<kRowThreads>(g, &tg, sh_scan);
+    const int xe = block_exclusive_scan<kRowThreads>(e, &te, sh_scan);
+    if (i < chunks) { c[2 * i] = carry_gt + xg; c[2 * i + 1] = carry_eq + xe; }
+    carry_gt += tg;
+    carry_eq += te;
+  }
+  if (threadIdx.x == 0) a.len[r] = a.top_k;
+}
+
+__global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chunks) {
+  __shared__ int sh_scan[kBigThreads / kWave];
+  const int r = blockIdx.y;
+  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
+  const BigState s = w.st[r];
+  if (!s.active) return;
+  const int shift = s.shift;
+  const uint64_t P = s.P;
+  const int n = a.s.q_pos[r] + 1;
+  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
+  if (lo >= hi) return;
+  const int* c = w.cnt + ((size_t)r * chunks + blockIdx.x) * 2;
+  // Keys above the threshold that precede this chunk, plus the equal keys taken before it.
+  const int gt_before = c[0], eq_before = c[1];
+  const int eq_taken_before = min(eq_before, s.need);
+  int carry_eq = eq_before, carry_out = gt_before + eq_taken_before;
+  const int K = a.top_k;
+  const float* row = a.scores + (size_t)r * a.ld;
+  int32_t* out = a.idx + (size_t)r * a.top_k;
+  for (int base = lo; base < hi; base += kBigThreads) {
+    const int t = base + threadIdx.x;
+    bool gt = false, eq = false;
+    if (t < hi) {
+      bool nn = false;
+      const uint64_t h = digit_prefix(order_key(row[t], nn), shift);
+      gt = h > P;
+      eq = h == P;
+    }
+    int tot_eq, tot_sel;
+    const int eq_rank = carry_eq + block_exclusive_scan<kBigThreads>(eq ? 1 : 0, &tot_eq, sh_scan);
+    const bool sel = gt || (eq && eq_rank < s.need);
+    const int at = carry_out + block_exclusive_scan<kBigThreads>(sel ? 1 : 0, &tot_sel, sh_scan);
+    if (sel && at < K) out[at] = t;
+    carry_eq += tot_eq;
+    carry_out += tot_sel;
+  }
+}
+
+bool lds_attr_set = false;
+
+}  // namespace
+
+static int big_chunks(const SeqView& s) { return (s.max_seq_len + kBigChunk - 1) / kBigChunk; }
+
+size_t topk_ws_bytes(const SeqView& s, int top_k) {
+  (void)top_k;
+  if (s.max_seq_len <= 4 * kCacheKeys) return 0;
+  const size_t rows = (size_t)s.total_q;
+  return round256(rows * sizeof(BigState)) + round256(rows * (1 << kMaxDigitBits) * 4) +
+         round256(rows * (size_t)big_chunks(s) * 2 * sizeof(int));
+}
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
+  const SeqView& s = a.s;
+  if (s.max_seq_len <= kCacheKeys) {
+    const size_t lds = (size_t)kCacheKeys * 4;
+    if (!lds_attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_row<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      lds_attr_set = true;
+    }
+    k_topk_row<true><<<s.total_q, kRowThreads, lds, st>>>(a);
+    return hipGetLastError();
+  }
+  if (s.max_seq_len <= 4 * kCacheKeys) {
+    k_topk_row<false><<<s.total_q, kRowThreads, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const int chunks = big_chunks(s);
+  const dim3 grid(chunks, s.total_q);
+  k_tkb_init<<<s.total_q, kBigThreads, 0, st>>>(a, chunks);
+  k_tkb_andor<<<grid, kBigThreads, 0, st>>>(a, chunks);
+  k_tkb_setup<<<s.total_q, 64, 0, st>>>(a, chunks);
+  for (int pass = 0; pass < 3; ++pass) {
+    k_tkb_hist<<<grid, kBigThreads, 0, st>>>(a, chunks);
+    k_tkb_pick<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
+  }
+  k_tkb_count<<<grid, kBigThreads, 0, st>>>(a, chunks);
+  k_tkb_scan<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
+  k_tkb_write<<<grid, kBigThreads, 0, st>>>(a, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace ml4

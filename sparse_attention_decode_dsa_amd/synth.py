@@ -260,3 +260,14 @@ def config(n: int, device="cpu", seed: Optional[int] = None, scale_down: int = 1
                          block_size=64, fmt="fp8", idx_heads=64, mla_heads=128,
                          layers=[layer_desc(0)], device=device)
     raise ValueError(n)
+
+
+def case_to(case: Case, device) -> Case:
+    """The same case with every tensor moved to `device` (data movement only)."""
+    out = Case(case.name, case.fmt, case.batch.to(device), case.idx_heads, case.mla_heads,
+               list(case.layers))
+    for l, li in case.inputs.items():
+        mv = lambda t: None if t is None else t.to(device)
+        out.inputs[l] = LayerInputs(mv(li.idx_pool), mv(li.q_idx), mv(li.q_idx_scale),
+                                    mv(li.w_idx), mv(li.lat_pool), mv(li.q_mla))
+    return out

@@ -1,0 +1,118 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the header
+declares, and its default-deny validation rejects bad calls -- listing every failed check
+-- without touching a GPU (nothing is launched when a check fails)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ml4dsa.h")
+
+M = pytest.importorskip("sparse_attention_decode_dsa_amd.ml4dsa",
+                        reason="libml4dsa.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ml4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert header_functions() == sorted(M.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(M.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding_and_pages():
+    text = open(HEADER).read()
+    def define(n):
+        return int(re.search(rf"#define {n} (\d+)", text).group(1))
+    assert define("ML4_IDX_ROW_FP8") == 132 and define("ML4_LAT_ROW_FP8") == 656
+    assert define("ML4_KV_LORA") == 512 and define("ML4_ROPE_DIM") == 64
+    assert define("ML4_MAX_TOPK") == 2048 and define("ML4_ABI_VERSION") == M.ML4_ABI_VERSION
+    assert M.ml4_abi_version() == M.ML4_ABI_VERSION
+
+
+def _seqs(**kw):
+    s = M.ml4_seqs()
+    s.batch, s.total_q, s.max_seq_len, s.max_q_per_seq = 1, 1, 4096, 1
+    s.block_size, s.max_blocks_per_seq = 64, 64
+    s.seq_lens = s.q_start = s.q_pos = s.block_table = 0x1000
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _cache(fmt, pool=0x10000):
+    c = M.ml4_cache()
+    c.pool, c.num_blocks, c.format = pool, 64, fmt
+    return c
+
+
+def test_indexer_default_deny_lists_every_reason():
+    s = _seqs(block_size=48, seq_lens=0)
+    rc = M.ml4_indexer_score(s, _cache(M.ML4_IDX_FP8_132, pool=0x10004), 0x2000, M.ML4_F32,
+                             None, None, 24, 0.0, 0x3000, 102, stream=0, check=False)
+    assert rc == M.ML4_E_INVALID
+    msg = M.ml4_last_error()
+    for needle in ["block_size must be a power of two", "seqs arrays", "16-byte aligned",
+                   "needs ML4_FP8_E4M3 queries", "w is NULL", "ld_scores < max_seq_len",
+                   "ld_scores must be a multiple of 4", "n_heads must be a multiple of 16"]:
+        assert needle in msg, (needle, msg)
+    assert len(msg.strip().splitlines()) >= 8
+
+
+def test_unsupported_and_workspace_codes():
+    s = _seqs()
+    rc = M.ml4_topk_select(s, 0x4000, 4096, 4096, 0x5000, 0x6000, stream=0, check=False)
+    assert rc == M.ML4_E_UNSUPPORTED and "top_k above 2048" in M.ml4_last_error()
+    big = _seqs(max_seq_len=1 << 20, max_blocks_per_seq=(1 << 20) // 64)
+    need = M.ml4_workspace_bytes(M.ML4_ENTRY_TOPK, big, 0, 2048)
+    assert need > 0
+    rc = M.ml4_topk_select(big, 0x4000, 1 << 20, 2048, 0x5000, 0x6000, None, 0, stream=0,
+                           check=False)
+    assert rc == M.ML4_E_WORKSPACE and "workspace" in M.ml4_last_error()
+
+
+def test_mla_default_deny():
+    s = _seqs()
+    rc = M.ml4_sparse_mla_decode(s, _cache(M.ML4_LAT_FP8_656), 0x7000, M.ML4_F32, 20, 32,
+                                 0x5000, None, 4096, -1.0, float("nan"), 0x8000, M.ML4_F32,
+                                 stream=0, check=False)
+    assert rc == M.ML4_E_INVALID
+    msg = M.ml4_last_error()
+    for needle in ["needs ML4_BF16 queries", "writes ML4_BF16 outputs",
+                   "n_heads must be a multiple of 16", "rope_dim must be 64 or 0",
+                   "topk_idx and topk_len", "top_k above 2048", "softmax_scale",
+                   "ssmax_s must be finite"]:
+        assert needle in msg, (needle, msg)
+
+
+def test_layer_modes_are_validated():
+    s = _seqs()
+    L = M.ml4_layer()
+    L.layer, L.kv_sharing_target_layer, L.topk_source_layer = 1, 1, 2
+    L.rope_dim, L.top_k, L.idx_heads, L.mla_heads = 64, 2048, 64, 128
+    L.softmax_scale = 0.04
+    caches = [_cache(M.ML4_LAT_FP8_656)] * 3
+    icaches = [_cache(M.ML4_IDX_FP8_132)] * 3
+    rc = M.ml4_sparse_attn_layer(L, s, caches, icaches, 0x100, M.ML4_FP8_E4M3, None, 0x100,
+                                 0x100, M.ML4_BF16, [0x100] * 3, [0x100] * 3, 0x100,
+                                 M.ML4_BF16, stream=0, check=False)
+    assert rc == M.ML4_E_INVALID
+    msg = M.ml4_last_error()
+    assert "kv_sharing_target_layer must be -1 or an earlier layer" in msg
+    assert "topk_source_layer must be -1 or an earlier layer" in msg
+
+
+def test_fault_query_rejects_null():
+    rc = M.LIB.ml4_fault_query(None, None, None)
+    assert rc == M.ML4_E_INVALID
