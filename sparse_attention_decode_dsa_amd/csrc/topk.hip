@@ -117,14 +117,67 @@ __device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_
 }
 
 // ------------------------------------------------------------------ one work-group per row
+// Scores are read as float4 (rows are 16-byte aligned and ld % 4 == 0, so the vector holding
+// the last candidate lies inside the row), U vectors per thread in flight per batch.
+constexpr int kU = 4;
+
+template <bool CACHE>
+__device__ __forceinline__ void load_keys(const float* row, const uint32_t* kc, int i4,
+                                          uint32_t k[4]) {
+  if (CACHE) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(kc + 4 * i4);
+    k[0] = v[0]; k[1] = v[1]; k[2] = v[2]; k[3] = v[3];
+  } else {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+    bool nn = false;
+    k[0] = order_key(v[0], nn); k[1] = order_key(v[1], nn);
+    k[2] = order_key(v[2], nn); k[3] = order_key(v[3], nn);
+  }
+}
+
+// Calls f(t, key) for every candidate t < n, threads striding over float4 vectors.
+template <bool CACHE, typename F>
+__device__ __forceinline__ void for_each_key(const float* row, const uint32_t* kc, int n, F&& f) {
+  const int n4 = (n + 3) >> 2;
+  for (int base = threadIdx.x; base < n4; base += kRowThreads * kU) {
+    uint32_t k[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+      if (i4 < n4) load_keys<CACHE>(row, kc, i4, k[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+      if (i4 >= n4) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * i4 + e < n) f(4 * i4 + e, k[u][e]);
+    }
+  }
+}
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 template <bool CACHE>
 __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   extern __shared__ uint32_t kcache[];
+  constexpr int NW = kRowThreads / kWave;
   __shared__ uint32_t hist[1 << kMaxDigitBits];
-  __shared__ int sh_scan[kRowThreads / kWave];
-  __shared__ uint32_t sh_and[kRowThreads / kWave], sh_or[kRowThreads / kWave];
+  __shared__ int sh_scan[NW];
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
   __shared__ int sh_sel[4];
   __shared__ int sh_nan;
+  __shared__ int sh_gt[NW], sh_eq[NW];
 
   const int r = blockIdx.x;
   int n = 0;
@@ -133,23 +186,35 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   const float* row = a.scores + (size_t)r * a.ld;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const int n4 = (n + 3) >> 2;
 
-  auto key_at = [&](int t) -> uint32_t {
-    if (CACHE) return kcache[t];
-    bool nn = false;
-    return order_key(row[t], nn);
-  };
-
-  // 1. common leading bits of every candidate key
+  // 1. common leading bits of every candidate key (and the LDS key cache)
   uint32_t av = ~0u, ov = 0u;
   bool any_nan = false;
-  for (int t = tid; t < n; t += kRowThreads) {
-    bool nn = false;
-    const uint32_t k = order_key(row[t], nn);
-    any_nan |= nn;
-    av &= k;
-    ov |= k;
-    if (CACHE) kcache[t] = k;
+  for (int base = tid; base < n4; base += kRowThreads * kU) {
+    f32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+      if (i4 < n4) v[u] = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+      if (i4 >= n4) continue;
+      uint32_t k[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool nn = false;
+        k[e] = order_key(v[u][e], nn);
+        if (4 * i4 + e < n) {
+          any_nan |= nn;
+          av &= k[e];
+          ov |= k[e];
+        }
+      }
+      if (CACHE) *reinterpret_cast<u32x4*>(kcache + 4 * i4) = u32x4{k[0], k[1], k[2], k[3]};
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -162,7 +227,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   if (any_nan) sh_nan = 1;
   av = ~0u; ov = 0u;
 #pragma unroll
-  for (int w = 0; w < kRowThreads / kWave; ++w) { av &= sh_and[w]; ov |= sh_or[w]; }
+  for (int w = 0; w < NW; ++w) { av &= sh_and[w]; ov |= sh_or[w]; }
   __syncthreads();
   if (tid == 0 && sh_nan) raise_fault(a.fault, kFaultNan);
 
@@ -178,10 +243,9 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
     const int nb = 1 << w;
     for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
     __syncthreads();
-    for (int t = tid; t < n; t += kRowThreads) {
-      const uint32_t k = key_at(t);
+    for_each_key<CACHE>(row, kcache, n, [&](int, uint32_t k) {
       if (digit_prefix(k, shift) == P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
-    }
+    });
     __syncthreads();
     find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
     const int d = sh_sel[0], above = sh_sel[1], cnt = sh_sel[2];
@@ -192,24 +256,73 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
     if (cnt == need) break;   // the whole bucket is selected
   }
 
-  // 3. ordered compaction
-  int32_t* out = a.idx + (size_t)r * K;
-  int carry_eq = 0, carry_out = 0;
-  for (int base = 0; base < n && carry_out < K; base += kRowThreads) {
-    const int t = base + tid;
-    bool gt = false, eq = false;
-    if (t < n) {
-      const uint64_t h = digit_prefix(key_at(t), shift);
-      gt = h > P;
-      eq = h == P;
+  // 3. ordered compaction: wave w owns a contiguous run of vectors; counts first, then an
+  //    in-order write with wave-level prefix sums (no block barrier inside the loop).
+  const int per = (n4 + NW - 1) / NW;
+  const int v_lo = wave * per, v_hi = min(n4, v_lo + per);
+  int gt_c = 0, eq_c = 0;
+  for (int base = v_lo + lane; base < v_hi; base += kWave * kU) {
+    uint32_t k[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kWave;
+      if (i4 < v_hi) load_keys<CACHE>(row, kcache, i4, k[u]);
     }
-    int tot_eq, tot_sel;
-    const int eq_rank = carry_eq + block_exclusive_scan<kRowThreads>(eq ? 1 : 0, &tot_eq, sh_scan);
-    const bool sel = gt || (eq && eq_rank < need);
-    const int at = carry_out + block_exclusive_scan<kRowThreads>(sel ? 1 : 0, &tot_sel, sh_scan);
-    if (sel && at < K) out[at] = t;
-    carry_eq += tot_eq;
-    carry_out += tot_sel;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kWave;
+      if (i4 >= v_hi) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (4 * i4 + e >= n) continue;
+        const uint64_t h = digit_prefix(k[u][e], shift);
+        gt_c += h > P;
+        eq_c += h == P;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) { gt_c += __shfl_xor(gt_c, m); eq_c += __shfl_xor(eq_c, m); }
+  if (lane == 0) { sh_gt[wave] = gt_c; sh_eq[wave] = eq_c; }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) { gt_before += sh_gt[w]; eq_before += sh_eq[w]; }
+  int32_t* out = a.idx + (size_t)r * K;
+  int carry_eq = eq_before;
+  int carry_out = gt_before + min(eq_before, need);
+  for (int i4 = v_lo + lane; i4 - lane < v_hi; i4 += kWave) {
+    uint32_t k[4] = {0u, 0u, 0u, 0u};
+    if (i4 < v_hi) load_keys<CACHE>(row, kcache, i4, k);
+    bool gt[4], eq[4];
+    int ne = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = i4 < v_hi && 4 * i4 + e < n;
+      const uint64_t h = digit_prefix(k[e], shift);
+      gt[e] = valid && h > P;
+      eq[e] = valid && h == P;
+      ne += eq[e];
+    }
+    const int eq_incl = wave_incl_scan(ne);
+    int eq_rank = carry_eq + eq_incl - ne;
+    bool sel[4];
+    int ns = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = gt[e] || (eq[e] && eq_rank < need);
+      eq_rank += eq[e];
+      ns += sel[e];
+    }
+    const int s_incl = wave_incl_scan(ns);
+    int at = carry_out + s_incl - ns;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sel[e]) {
+        if (at < K) out[at] = 4 * i4 + e;
+        ++at;
+      }
+    carry_eq += __shfl(eq_incl, kWave - 1);
+    carry_out += __shfl(s_incl, kWave - 1);
   }
   if (tid == 0) a.len[r] = K;
 }
