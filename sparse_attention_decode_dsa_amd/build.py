@@ -37,13 +37,19 @@ def _run(cmd):
     return out
 
 
+# Per-source extras: the indexer's MFMA results feed VALU work directly, so they are kept
+# in VGPRs rather than accumulation registers (no copy per element).
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        jobs.append((obj, [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+                           "-o", obj]))
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))
     tmp = LIB + ".tmp"

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
 #pragma unroll
           for (int c = 0; c < 4; ++c) d = mfma_f16(qa[ht][c], kb[c], d);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += wq[ht][i] * fmaxf(d[i], 0.f);
+          for (int i = 0; i < 4; ++i) part = fmaf(wq[ht][i], relu_bits(d[i]), part);
         }
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);

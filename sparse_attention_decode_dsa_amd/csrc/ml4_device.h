@@ -65,6 +65,13 @@ __device__ __forceinline__ bf16x4 e4m3x4_to_bf16(uint32_t w) {
   return r;
 }
 
+// ReLU as one integer max on the IEEE bits: negative floats (sign bit set) compare below
+// 0, -0 maps to +0, non-negative values are unchanged.  (A float max would first quiet
+// signalling NaNs with an extra instruction per element.)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));

@@ -36,48 +36,143 @@ namespace {
 
 constexpr int kLatRow = 656;
 constexpr int kTK = 32;            // keys per tile
-constexpr int kKS = 584;           // bf16 stride of a key row of the QK tile (576 + 8)
-constexpr int kVS = 520;           // fp16 stride of a key row of the PV tile (512 + 8)
+constexpr int kKS = 584;           // fp16 stride of a key row of the tile (576 + 8)
 constexpr float kRescaleSlack = 8.0f;
 constexpr uint32_t kFaultBlock = 1u << 0;
 constexpr uint32_t kFaultTopk = 1u << 1;
 constexpr uint32_t kFaultQpos = 1u << 3;
+constexpr uint32_t kFaultRange = 1u << 4;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) short lds_short;
 
-struct Gathered {
-  u32x4 lat[4];   // 64 e4m3 codes
-  u32x4 rope;     // 8 bf16
-  float scale;
-  int ok;
-};
+constexpr int kNStage = 3;         // raw gather ring: the tile being staged + two in flight
+constexpr float kF16Max = 65504.0f;
+constexpr int kMaxSplitKeys = 2048;   // top_k <= 2048
 
-constexpr int kMlaWaves = 4;
-constexpr int kMlaHT = 1;                 // 16-head tiles per wave
-constexpr int kHeadsPerWg = kMlaWaves * 16 * kMlaHT;
+// Waits until at most n of this wave's vector-memory operations are outstanding (vmcnt).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (bits 6:4) and lgkmcnt
+  // (bits 11:8) left at their maxima so only vmcnt is waited on.
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-template <int ROPE, int WAVES, int HT>
-__global__ __launch_bounds__(WAVES * kWave) void k_mla_fp8(MlaLaunch a, int nsplit,
-                                                           int keys_per_split, float* part) {
-  constexpr int NT = WAVES * kWave;
-  constexpr int NC = (512 + ROPE) / 32;        // 32-wide K chunks of the QK product
-  __shared__ __attribute__((aligned(16))) __bf16 ks_tile[kTK * kKS];
-  __shared__ __attribute__((aligned(16))) _Float16 vs_tile[kTK * kVS];
-  __shared__ float sc_tile[kTK * 4];
-  __shared__ int ok_tile[kTK];
+// Work split inside a work-group of 8 waves (one query row, up to 128 heads):
+//   wave w owns head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half
+//   dh = w >> 2.  QK: it contracts its half of the 576 (NoPE: 512) dims for its 32 heads and
+//   adds the partner wave's (w ^ 4) partial through LDS, so both hold the full scores.  PV:
+//   it accumulates O for its 32 heads over latent dims 256 dh .. 256 dh + 255.  Every K or V
+//   fragment read from LDS feeds two MFMAs; per wave the query takes 72 registers and the
+//   accumulator 128.
+constexpr int kMlaThreads = 512;
+constexpr int kMlaWaves = 8;
+constexpr int kHeadsPerWg = 128;
+
+// Partial S^T of key sub-tile kt over this wave's chunks: rows = keys 16 kt + 4 g + j,
+// columns = heads; each 128-dim block is summed on its own and multiplied by its key's scale
+// (RoPE chunks: 1).
+template <int ROPE, int DH>
+__device__ __forceinline__ void qk_half(const _Float16* ks_tile, const float* sc_tile,
+                                        const f16x8 (&qb)[2][(512 + ROPE) / 64], int kt,
+                                        f32x4 (&sk)[2], int g16, int c16) {
+  constexpr int NH = (512 + ROPE) / 64;      // chunks per half: 9 or 8
+  const _Float16* krow = ks_tile + (kt * 16 + c16) * kKS + 8 * g16;
+  f32x4 tmp[2];
+  tmp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  tmp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sk[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sk[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int c = DH * NH + i;
+    const int blk = c < 16 ? c / 4 : 4;
+    const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 32 * c);
+    tmp[0] = mfma_f16(ka, qb[0][i], tmp[0]);
+    tmp[1] = mfma_f16(ka, qb[1][i], tmp[1]);
+    const int next_blk = (i + 1 < NH) ? ((c + 1) < 16 ? (c + 1) / 4 : 4) : -1;
+    if (next_blk != blk) {                       // block ends here: fold it in
+      if (blk < 4) {
+        const f32x4 scl{sc_tile[(kt * 16 + 4 * g16 + 0) * 4 + blk], sc_tile[(kt * 16 + 4 * g16 + 1) * 4 + blk],
+                        sc_tile[(kt * 16 + 4 * g16 + 2) * 4 + blk], sc_tile[(kt * 16 + 4 * g16 + 3) * 4 + blk]};
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sk[ht][j] = fmaf(tmp[ht][j], scl[j], sk[ht][j]);
+      } else {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) sk[ht] += tmp[ht];
+      }
+      tmp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tmp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// O^T[256 dh .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.
+template <int DH>
+__device__ __forceinline__ void pv_half(const _Float16* ks_tile, const float* sc_tile,
+                                        const float (&pv)[2][2][4], f32x4 (&o_acc)[2][16],
+                                        int g16, int c16) {
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+    const int blk = 2 * DH + b2;
+    float vsc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vsc[e] = sc_tile[((e >> 2) * 16 + 4 * g16 + (e & 3)) * 4 + blk];
+    f16x8 pb[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int dt = blk * 8 + dd;          // global 16-dim tile
+      // lane (g, i) supplies keys {4g + i/4} x dims {16 dt + 4 (i%4) .. +3}; receives dim
+      // 16 dt + i of keys 4g .. 4g+3 (then 16 + 4g .. 16 + 4g + 3).
+      const _Float16* src0 = ks_tile + (4 * g16 + (c16 >> 2)) * kKS + 16 * dt + 4 * (c16 & 3);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0 + 16 * kKS)));
+      const s16x8 w8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const f16x8 va = __builtin_bit_cast(f16x8, w8);
+      o_acc[0][b2 * 8 + dd] = mfma_f16(va, pb[0], o_acc[0][b2 * 8 + dd]);
+      o_acc[1][b2 * 8 + dd] = mfma_f16(va, pb[1], o_acc[1][b2 * 8 + dd]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int ROPE>
+__global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit,
+                                                         int keys_per_split, float* part) {
+  constexpr int NT = kMlaThreads;
+  constexpr int NCH = ROPE ? 41 : 33;            // 16-byte chunks read per row (NoPE: no RoPE)
+  constexpr int NH = (512 + ROPE) / 64;          // 32-wide K chunks per dim half
+  constexpr int RAW = kTK * NCH;                 // chunks per tile
+  constexpr int PER_WAVE = (RAW + NT - 1) / NT;
+  constexpr int STAGE_CHUNKS = PER_WAVE * NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* raw = smem;                                          // [kNStage][STAGE_CHUNKS][16]
+  _Float16* ks_tile = reinterpret_cast<_Float16*>(raw + kNStage * STAGE_CHUNKS * 16);  // [kTK][kKS]
+  float* sc_tile = reinterpret_cast<float*>(ks_tile + kTK * kKS);                      // [kTK][4]
+  float* xs = sc_tile + kTK * 4;                                                       // [8][16][64]
+  int* ok_tile = reinterpret_cast<int*>(xs + kMlaWaves * 16 * kWave);                  // [kTK]
+  int* slot_sh = ok_tile + kTK;                                                        // [keys]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int g16 = lane >> 4, c16 = lane & 15;
+  const int hg = wave & 3, dh = wave >> 2;
   const int r = blockIdx.x;
-  const int h0 = blockIdx.y * (WAVES * 16 * HT) + wave * 16 * HT;
+  const int h0 = blockIdx.y * kHeadsPerWg + hg * 32;
   const int split = blockIdx.z;
   const SeqView& s = a.s;
   const int H = a.n_heads;
   const int b = request_of(s.q_start, s.batch, r);
-  int p = s.q_pos[r];
+  const int p = s.q_pos[r];
   bool row_ok = true;
   if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len) {
     if (tid == 0 && blockIdx.y == 0 && split == 0) raise_fault(a.fault, kFaultQpos);
@@ -91,170 +186,164 @@ __global__ __launch_bounds__(WAVES * kWave) void k_mla_fp8(MlaLaunch a, int nspl
   if (!row_ok) nsel = 0;
   const int k_begin = split * keys_per_split;
   const int k_end = min(nsel, k_begin + keys_per_split);
-  const int ntiles = k_end > k_begin ? (k_end - k_begin + kTK - 1) / kTK : 0;
+  const int nkeys = max(0, k_end - k_begin);
+  const int ntiles = (nkeys + kTK - 1) / kTK;
 
-  // Waves whose heads lie past n_heads only gather.  (n_heads is a multiple of 16.)
-  const bool active = h0 < H;
-  // Query fragments: B operand of S^T = K Q^T (column = head, K = latent/RoPE dims).
-  bf16x8 qb[HT][NC];
-  const __bf16* q = static_cast<const __bf16*>(a.q);
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int hq = active ? h0 + ht * 16 + c16 : c16;
-    const __bf16* qh = q + ((size_t)r * H + hq) * (512 + ROPE) + 8 * g16;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qb[ht][c] = *reinterpret_cast<const bf16x8*>(qh + 32 * c);
-  }
-  const float qk_scale =
-      a.softmax_scale * ssmax_mult(a.ssmax_s, row_ok ? p : 0) * kLog2e;
-
-  f32x4 o_acc[HT][32];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) o_acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[HT], l_part[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) { m_run[ht] = -__builtin_inff(); l_part[ht] = 0.f; }
-
+  // Physical slot of every selected key of this split (-1: outside [0, p] or bad block).
   const int32_t* sel = a.idx + (size_t)r * a.top_k;
   const int32_t* bt = s.block_table + (size_t)b * s.mbps;
-  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
-  const int bs_mask = (1 << s.lbs) - 1;
-
-  // Each thread gathers 64 latent codes (+8 RoPE values, +1 scale) of one key per item.
-  constexpr int kItems = (kTK * 8 + NT - 1) / NT;
-  Gathered gq[kItems];
-  auto gather = [&](int tile) {
-#pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      const int u = tid + it * NT;
-      Gathered& G = gq[it];
-      G.ok = 0;
-      G.scale = 0.f;
-      if (u >= kTK * 8) continue;
-      const int kk = u >> 3, part = u & 7;
-      const int i = k_begin + tile * kTK + kk;
-      if (i >= k_end) continue;
-      const int t = sel[i];
+  for (int i = tid; i < ntiles * kTK; i += NT) {
+    int slot = -1;
+    if (i < nkeys) {
+      const int t = sel[k_begin + i];
       if (t < 0 || t > p) {
-        if (part == 0) raise_fault(a.fault, kFaultTopk);
-        continue;
+        raise_fault(a.fault, kFaultTopk);
+      } else {
+        const int blk = bt[t >> s.lbs];
+        if ((unsigned)blk >= (unsigned long long)a.num_blocks)
+          raise_fault(a.fault, kFaultBlock);
+        else
+          slot = (blk << s.lbs) | (t & ((1 << s.lbs) - 1));
       }
-      const int blk = bt[t >> s.lbs];
-      if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
-        if (part == 0) raise_fault(a.fault, kFaultBlock);
-        continue;
-      }
-      const uint8_t* rp = pool + (((int64_t)blk << s.lbs) + (t & bs_mask)) * kLatRow;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) G.lat[v] = *reinterpret_cast<const u32x4*>(rp + 64 * part + 16 * v);
-      if (ROPE) G.rope = *reinterpret_cast<const u32x4*>(rp + 528 + 16 * part);
-      if (part < 4) G.scale = *reinterpret_cast<const float*>(rp + 512 + 4 * part);
-      G.ok = 1;
     }
-  };
-  auto stage = [&]() {
+    slot_sh[i] = slot;
+  }
+  __syncthreads();
+
+  // Gather: instruction m of a tile moves chunks 64m .. 64m+63 of the tile's rows straight
+  // into LDS (chunk f = key f / NCH, bytes 16 (f % NCH) of its row); lanes past the tile or
+  // on a masked key read the pool's first chunk instead, which staging ignores.
+  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
+  auto issue = [&](int tile) {
+    unsigned char* dst = raw + (tile % kNStage) * STAGE_CHUNKS * 16;
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      const int u = tid + it * NT;
-      if (u >= kTK * 8) continue;
-      const Gathered& G = gq[it];
-      const int kk = u >> 3, part = u & 7;
-      __bf16* dst = ks_tile + kk * kKS + 64 * part;
-      _Float16* vdst = vs_tile + kk * kVS + 64 * part;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 x;
-          f16x8 y;
-          if (G.ok) {
-            const bf16x4 lo = e4m3x4_to_bf16(G.lat[v][2 * h]);
-            const bf16x4 hi = e4m3x4_to_bf16(G.lat[v][2 * h + 1]);
-            x = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const f16x4 flo = e4m3x4_to_f16(G.lat[v][2 * h]);
-            const f16x4 fhi = e4m3x4_to_f16(G.lat[v][2 * h + 1]);
-            y = f16x8{flo[0], flo[1], flo[2], flo[3], fhi[0], fhi[1], fhi[2], fhi[3]};
-          } else {
-            x = bf16x8{};
-            y = f16x8{};
-          }
-          *reinterpret_cast<bf16x8*>(dst + 16 * v + 8 * h) = x;
-          *reinterpret_cast<f16x8*>(vdst + 16 * v + 8 * h) = y;
-        }
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int m = wave + u * kMlaWaves;
+      const int f = m * kWave + lane;
+      const uint8_t* src = pool;
+      if (f < RAW) {
+        const int kk = f / NCH, j = f - (f / NCH) * NCH;
+        const int slot = slot_sh[tile * kTK + kk];
+        if (slot >= 0) src = pool + (int64_t)slot * kLatRow + 16 * j;
       }
-      if (ROPE) {
-        u32x4 rv = G.ok ? G.rope : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(ks_tile + kk * kKS + 512 + 8 * part) = rv;
-      }
-      if (part < 4) sc_tile[kk * 4 + part] = G.ok ? G.scale : 0.f;
-      if (part == 0) ok_tile[kk] = G.ok;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(dst + (size_t)m * kWave * 16), 16, 0, 0);
     }
   };
 
-  if (ntiles > 0) gather(0);
+  // Query fragments for this wave's 32 heads and dim half (B operand of S^T = K Q^T).
+  const bool ht_live[2] = {h0 < H, h0 + 16 < H};
+  const bool active = ht_live[0];
+  f16x8 qb[2][NH];
+  bool q_range = true;
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int hq = ht_live[ht] ? h0 + 16 * ht + c16 : c16;
+    const __bf16* qh = static_cast<const __bf16*>(a.q) + ((size_t)r * H + hq) * (512 + ROPE) +
+                       8 * g16 + 32 * NH * dh;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)v[e];
+        q_range &= fabsf(f) <= kF16Max;
+        qb[ht][i][e] = (_Float16)f;      // exact for bf16 values inside the fp16 range
+      }
+    }
+  }
+  if (__any(!q_range) && active && lane == 0) raise_fault(a.fault, kFaultRange);
+  const float qk_scale = a.softmax_scale * ssmax_mult(a.ssmax_s, row_ok ? p : 0) * kLog2e;
+
+  f32x4 o_acc[2][16];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o_acc[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l_part[2] = {0.f, 0.f};
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
   for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();   // the previous tile's readers are done
-    stage();
-    __syncthreads();
-    if (tile + 1 < ntiles) gather(tile + 1);   // in flight during this tile's math
-    if (!active) continue;
+    if (tile + 2 < ntiles) issue(tile + 2);
+    const int ahead = min(2, ntiles - 1 - tile);
+    if (ahead == 2) wait_vmcnt<2 * PER_WAVE>();
+    else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // every wave's chunks of this tile are in LDS; last tile's math done
 
-    // ---- S^T = K Q^T : two 16-key sub-tiles x HT 16-head tiles
-    f32x4 sacc[2][HT];
+    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key flags
+    {
+      const unsigned char* src = raw + (tile % kNStage) * STAGE_CHUNKS * 16;
+      for (int f = tid; f < RAW; f += NT) {
+        const int kk = f / NCH, j = f - (f / NCH) * NCH;
+        const bool ok = slot_sh[tile * kTK + kk] >= 0;
+        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * f) : u32x4{0, 0, 0, 0};
+        if (j < 32) {
+          _Float16* kd = ks_tile + kk * kKS + 16 * j;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const __bf16* krow = ks_tile + (kt * 16 + c16) * kKS + 8 * g16;
-      float kscale[4][4];
+          for (int h = 0; h < 2; ++h) {
+            const f16x4 f0 = e4m3x4_to_f16(v[2 * h]), f1 = e4m3x4_to_f16(v[2 * h + 1]);
+            *reinterpret_cast<f16x8*>(kd + 8 * h) =
+                f16x8{f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+          }
+          if (j == 0) ok_tile[kk] = ok;
+        } else if (j == 32) {
+          *reinterpret_cast<u32x4*>(sc_tile + kk * 4) = v;
+        } else {
+          const bf16x8 rb = __builtin_bit_cast(bf16x8, v);
+          f16x8 rh;
+          bool in_range = true;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int bl = 0; bl < 4; ++bl) kscale[j][bl] = sc_tile[(kt * 16 + 4 * g16 + j) * 4 + bl];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) sacc[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int bl = 0; bl < 4; ++bl) {
-        f32x4 tmp[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) tmp[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 32 * (4 * bl + c));
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) tmp[ht] = mfma_bf16(ka, qb[ht][4 * bl + c], tmp[ht]);
-        }
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sacc[kt][ht][j] = fmaf(tmp[ht][j], kscale[j][bl], sacc[kt][ht][j]);
-      }
-      if (ROPE) {
-#pragma unroll
-        for (int c = 16; c < NC; ++c) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 32 * c);
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) sacc[kt][ht] = mfma_bf16(ka, qb[ht][c], sacc[kt][ht]);
+          for (int e = 0; e < 8; ++e) {
+            const float f2 = (float)rb[e];
+            in_range &= fabsf(f2) <= kF16Max;
+            rh[e] = (_Float16)f2;
+          }
+          if (!in_range) raise_fault(a.fault, kFaultRange);
+          *reinterpret_cast<f16x8*>(ks_tile + kk * kKS + 512 + 8 * (j - 33)) = rh;
         }
       }
     }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- online softmax (base 2) per head; lane column = head, rows = keys 4*g16 + j
-    bool okk[2][4];
+    // ---- partial S^T over this wave's dim half per key sub-tile, exchanged through LDS;
+    //      both partner waves then add half 0 + half 1 in the same order
+    {
+      f32x4* mine = reinterpret_cast<f32x4*>(xs + wave * 16 * kWave);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 sk[2];
+        if (dh == 0) qk_half<ROPE, 0>(ks_tile, sc_tile, qb, kt, sk, g16, c16);
+        else qk_half<ROPE, 1>(ks_tile, sc_tile, qb, kt, sk, g16, c16);
+        mine[(2 * kt) * kWave + lane] = sk[0];
+        mine[(2 * kt + 1) * kWave + lane] = sk[1];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    f32x4 sacc[2][2];
+    {
+      const f32x4* h0p = reinterpret_cast<const f32x4*>(xs + (wave & 3) * 16 * kWave);
+      const f32x4* h1p = reinterpret_cast<const f32x4*>(xs + ((wave & 3) | 4) * 16 * kWave);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) okk[kt][j] = ok_tile[kt * 16 + 4 * g16 + j] != 0;
-    float pv[2][HT][4];
+      for (int q4 = 0; q4 < 4; ++q4) sacc[q4 >> 1][q4 & 1] = h0p[q4 * kWave + lane] + h1p[q4 * kWave + lane];
+    }
+
+    // ---- online softmax (base 2) per head (lane column), identical in both partner waves
+    float pv[2][2][4];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
+    for (int ht = 0; ht < 2; ++ht) {
       float mt = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = okk[kt][j] ? sacc[kt][ht][j] * qk_scale : -__builtin_inff();
-          pv[kt][ht][j] = v;
+          const float v = ok_tile[kt * 16 + 4 * g16 + j] ? sacc[kt][ht][j] * qk_scale
+                                                         : -__builtin_inff();
+          pv[ht][kt][j] = v;
           mt = fmaxf(mt, v);
         }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -265,82 +354,65 @@ __global__ __launch_bounds__(WAVES * kWave) void k_mla_fp8(MlaLaunch a, int nspl
         const float alpha = (m_run[ht] == -__builtin_inff()) ? 0.f : exp2f(m_run[ht] - m_new);
         l_part[ht] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) o_acc[ht][dt] *= alpha;
+        for (int i = 0; i < 16; ++i) o_acc[ht][i] *= alpha;
         m_run[ht] = m_new;
       }
-      const float m_use = m_run[ht];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float e = (m_use == -__builtin_inff()) ? 0.f : exp2f(pv[kt][ht][j] - m_use);
-          pv[kt][ht][j] = e;
+          const float e = (m_run[ht] == -__builtin_inff()) ? 0.f : exp2f(pv[ht][kt][j] - m_run[ht]);
+          pv[ht][kt][j] = e;
           l_part[ht] += e;
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O^T += V^T P^T, per 128-column block of V with its scale folded into P
-#pragma unroll
-    for (int bl = 0; bl < 4; ++bl) {
-      f16x8 pb[HT];
-      float vs[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vs[kt][j] = sc_tile[(kt * 16 + 4 * g16 + j) * 4 + bl];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)(pv[e >> 2][ht][e & 3] * vs[e >> 2][e & 3]);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int dt = bl * 8 + dd;
-        // lane (g, i) supplies keys {4g + i/4} x dims {16 dt + 4 (i%4) .. +3}; receives dim
-        // 16 dt + i of keys 4g .. 4g+3 (then 16 + 4g .. 16 + 4g + 3).
-        const _Float16* src0 = vs_tile + (4 * g16 + (c16 >> 2)) * kVS + 16 * dt + 4 * (c16 & 3);
-        const _Float16* src1 = src0 + 16 * kVS;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src1)));
-        const s16x8 w8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const f16x8 va = __builtin_bit_cast(f16x8, w8);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o_acc[ht][dt] = mfma_f16(va, pb[ht], o_acc[ht][dt]);
-      }
-    }
+    // ---- O^T += V^T P^T over this wave's dim half
+    if (dh == 0) pv_half<0>(ks_tile, sc_tile, pv, o_acc, g16, c16);
+    else pv_half<1>(ks_tile, sc_tile, pv, o_acc, g16, c16);
   }
 
-  // ---- epilogue: lane (g, i) holds O[head h0 + 16 ht + i][dims 16 dt + 4 g + j]
+  // ---- epilogue: lane (g, i) holds O[head h0 + 16 ht + i][dims 256 dh + 16 t + 4 g + j]
   if (!active) return;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
+  for (int ht = 0; ht < 2; ++ht) {
+    if (!ht_live[ht]) continue;
     float l = l_part[ht];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int h = h0 + ht * 16 + c16;
+    const int h = h0 + 16 * ht + c16;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse2 = l > 0.f ? m_run[ht] + log2f(l) : -__builtin_inff();
+    const int d0 = 256 * dh + 4 * g16;
     if (nsplit == 1) {
-      __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)r * H + h) * 512 + 4 * g16;
+      __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)r * H + h) * 512 + d0;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 v = o_acc[ht][dt] * inv;
-        *reinterpret_cast<bf16x4*>(out + 16 * dt) =
+      for (int i = 0; i < 16; ++i) {
+        const f32x4 v = o_acc[ht][i] * inv;
+        *reinterpret_cast<bf16x4*>(out + 16 * i) =
             bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
-      if (a.lse && g16 == 0) a.lse[(size_t)r * H + h] = lse2 * kLn2;
+      if (a.lse && g16 == 0 && dh == 0) a.lse[(size_t)r * H + h] = lse2 * kLn2;
     } else {
       float* po = part + (((size_t)r * H + h) * nsplit + split) * 513;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 v = o_acc[ht][dt] * inv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) po[16 * dt + 4 * g16 + j] = v[j];
+      for (int i = 0; i < 16; ++i) {
+        const f32x4 v = o_acc[ht][i] * inv;
+        *reinterpret_cast<f32x4*>(po + d0 + 16 * i) = v;
       }
-      if (g16 == 0) po[512] = lse2;
+      if (g16 == 0 && dh == 0) po[512] = lse2;
     }
   }
+}
+
+template <int ROPE>
+constexpr size_t mla_lds_bytes() {
+  constexpr int NCH = ROPE ? 41 : 33;
+  constexpr int RAW = kTK * NCH;
+  constexpr int PER_WAVE = (RAW + kMlaThreads - 1) / kMlaThreads;
+  return (size_t)kNStage * PER_WAVE * kMlaThreads * 16 + (size_t)kTK * kKS * 2 + kTK * 4 * 4 +
+         kMlaWaves * 16 * kWave * 4 + kTK * 4 + kMaxSplitKeys * 4;
 }
 
 // Merge split partials: o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) (base-2 lse).
@@ -459,6 +531,8 @@ struct MlaPlan {
   int groups, nsplit, keys_per_split;
 };
 
+// One work-group per (row, 128 heads, key split); splits only when the grid would leave
+// CUs idle.
 MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
   MlaPlan pl{};
   pl.groups = (H + kHeadsPerWg - 1) / kHeadsPerWg;
@@ -475,9 +549,16 @@ MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
 
 template <int ROPE>
 hipError_t launch_fp8(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
+  constexpr size_t lds = mla_lds_bytes<ROPE>();
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8<ROPE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   dim3 grid(a.s.total_q, pl.groups, pl.nsplit);
-  k_mla_fp8<ROPE, kMlaWaves, kMlaHT><<<grid, kMlaWaves * kWave, 0, st>>>(a, pl.nsplit,
-                                                                        pl.keys_per_split, part);
+  k_mla_fp8<ROPE><<<grid, kMlaThreads, lds, st>>>(a, pl.nsplit, pl.keys_per_split, part);
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ import os
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libml4dsa.so")
+# ML4DSA_LIB selects another build of the same library (A/B timing); default: in-tree build.
+LIB_PATH = os.environ.get("ML4DSA_LIB") or os.path.join(PKG, "libml4dsa.so")
 
 # ---- constants mirrored from include/ml4dsa.h
 ML4_ABI_VERSION = 1
@@ -22,6 +23,7 @@ ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
 ML4_IDX_F32, ML4_IDX_FP8_132 = 0, 1
 ML4_LAT_F32, ML4_LAT_FP8_656 = 0, 1
 ML4_FAULT_BLOCK_ID, ML4_FAULT_TOPK_INDEX, ML4_FAULT_NAN_SCORE, ML4_FAULT_QPOS = 1, 2, 4, 8
+ML4_FAULT_RANGE = 16
 ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",

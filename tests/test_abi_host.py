@@ -39,6 +39,9 @@ def test_header_constants_match_binding_and_pages():
     assert define("ML4_KV_LORA") == 512 and define("ML4_ROPE_DIM") == 64
     assert define("ML4_MAX_TOPK") == 2048 and define("ML4_ABI_VERSION") == M.ML4_ABI_VERSION
     assert M.ml4_abi_version() == M.ML4_ABI_VERSION
+    bits = {m.group(1): 1 << int(m.group(2))
+            for m in re.finditer(r"(ML4_FAULT_\w+) = 1u << (\d+)", text)}
+    assert bits and all(getattr(M, k) == v for k, v in bits.items())
 
 
 def _seqs(**kw):
