@@ -77,7 +77,8 @@ enum ml4_fault_bits {
   ML4_FAULT_NAN_SCORE = 1u << 2,   /* a candidate score was NaN (ranked below -inf)        */
   ML4_FAULT_QPOS = 1u << 3,        /* q_pos outside [0, seq_len) or > max_seq_len - 1      */
   ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a bf16 query or RoPE key element beyond the
-                                      fp16 range (|x| > 65504) or NaN; that row's output
+                                      fp16 range (|x| > 65504) or NaN, or a selected key's
+                                      latent scale with |s| > 128 or NaN; that row's output
                                       is unspecified                                       */
 };
 

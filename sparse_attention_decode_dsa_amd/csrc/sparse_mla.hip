@@ -8,23 +8,24 @@
 // positions become global cache slots, one entry per query token); Long context › DCP
 // (partial attentions merged through their log-sum-exp).
 //
-// One work-group = one query row x a group of heads x a contiguous range of its selected
-// keys.  Per 32-key tile:
-//   gather  the selected 656-byte rows (slot = block_table[t / bs] * bs + t % bs) with 16-byte
-//           loads, decode the e4m3 codes exactly to bf16 and store [key][576] in LDS, keeping
-//           the four per-128 scales in fp32 beside them (the RoPE part is already bf16; a
-//           NoPE layer never touches those bytes);
-//   QK      S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 with keys on M and heads on N, the query
-//           fragments resident in registers; each 128-column block is accumulated on its
-//           own and multiplied by its key's scale in fp32;
-//   softmax online, base 2, per head = per lane column; the running maximum is only moved
-//           when a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled;
+// One work-group = one query row x up to 128 heads x a contiguous range of its selected
+// keys, 8 waves.  Per 32-key tile:
+//   gather  the selected 656-byte rows (slot = block_table[t / bs] * bs + t % bs) straight
+//           into an LDS ring with 16-byte global->LDS transfers, two tiles ahead of the math;
+//   stage   decode the e4m3 codes exactly to fp16 into a [key][576] tile (the bf16 RoPE part
+//           is rounded to fp16; a value beyond the fp16 range is reported), keep the four
+//           per-128 scales in fp32 beside it (a NoPE layer never touches the RoPE bytes);
+//   QK      S^T = K . Q^T on v_mfma_f32_16x16x32_f16 with keys on M and heads on N; each wave
+//           contracts one half of the latent dims (its two 128-dim scale blocks, each summed
+//           on its own and multiplied by its key's scale in fp32) plus half of the RoPE dims,
+//           for 32 heads; the partner wave's half arrives through LDS;
+//   softmax online, base 2, per head = per lane column; the running maximum only moves when
+//           a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled;
 //   PV      O^T = V^T . P^T on v_mfma_f32_16x16x32_f16 with latent columns on M, heads on
-//           N: the V^T fragments come from a second [key][512] fp16 copy of the tile through
+//           N, over the wave's 256 latent dims: V^T fragments come from the fp16 tile through
 //           ds_read_b64_tr_b16, P^T comes from the QK accumulators in place (the key order of
 //           both operands is the same permutation), and the per-128 scale of V is folded into
-//           P per column block.  fp16 rather than bf16 for this product: e4m3 values are exact
-//           in both, and P keeps 11 significant bits instead of 8, which bounds the output
+//           P per column block.  fp16 keeps 11 significant bits of P, which bounds the output
 //           error by 2^-11 * sum_t p_t |c_t| even when SSMax makes the softmax peaked.
 // A row's selected keys may be split across work-groups; the partial results are merged by
 // their log-sum-exp in a second kernel.
@@ -37,7 +38,9 @@ namespace {
 constexpr int kLatRow = 656;
 constexpr int kTK = 32;            // keys per tile
 constexpr int kKS = 584;           // fp16 stride of a key row of the tile (576 + 8)
+constexpr int kQRS = 72;           // fp16 stride of a head's RoPE query in LDS (64 + 8)
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kMaxVScale = 128.0f;   // 2^8 * 128 * 448 stays inside fp16 after P * scale
 constexpr uint32_t kFaultBlock = 1u << 0;
 constexpr uint32_t kFaultTopk = 1u << 1;
 constexpr uint32_t kFaultQpos = 1u << 3;
@@ -46,9 +49,12 @@ constexpr uint32_t kFaultRange = 1u << 4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) short lds_short;
 
-constexpr int kNStage = 3;         // raw gather ring: the tile being staged + two in flight
+constexpr int kNStage = 3;         // gather ring: the tile being staged + two in flight
 constexpr float kF16Max = 65504.0f;
 constexpr int kMaxSplitKeys = 2048;   // top_k <= 2048
+constexpr int kMlaThreads = 512;
+constexpr int kMlaWaves = 8;
+constexpr int kHeadsPerWg = 128;
 
 // Waits until at most n of this wave's vector-memory operations are outstanding (vmcnt).
 template <int N>
@@ -58,79 +64,114 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Work split inside a work-group of 8 waves (one query row, up to 128 heads):
-//   wave w owns head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half
-//   dh = w >> 2.  QK: it contracts its half of the 576 (NoPE: 512) dims for its 32 heads and
-//   adds the partner wave's (w ^ 4) partial through LDS, so both hold the full scores.  PV:
-//   it accumulates O for its 32 heads over latent dims 256 dh .. 256 dh + 255.  Every K or V
-//   fragment read from LDS feeds two MFMAs; per wave the query takes 72 registers and the
-//   accumulator 128.
-constexpr int kMlaThreads = 512;
-constexpr int kMlaWaves = 8;
-constexpr int kHeadsPerWg = 128;
-
-// Partial S^T of key sub-tile kt over this wave's chunks: rows = keys 16 kt + 4 g + j,
-// columns = heads; each 128-dim block is summed on its own and multiplied by its key's scale
-// (RoPE chunks: 1).
-template <int ROPE, int DH>
-__device__ __forceinline__ void qk_half(const _Float16* ks_tile, const float* sc_tile,
-                                        const f16x8 (&qb)[2][(512 + ROPE) / 64], int kt,
-                                        f32x4 (&sk)[2], int g16, int c16) {
-  constexpr int NH = (512 + ROPE) / 64;      // chunks per half: 9 or 8
-  const _Float16* krow = ks_tile + (kt * 16 + c16) * kKS + 8 * g16;
-  f32x4 tmp[2];
-  tmp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tmp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sk[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sk[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    const int c = DH * NH + i;
-    const int blk = c < 16 ? c / 4 : 4;
-    const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 32 * c);
-    tmp[0] = mfma_f16(ka, qb[0][i], tmp[0]);
-    tmp[1] = mfma_f16(ka, qb[1][i], tmp[1]);
-    const int next_blk = (i + 1 < NH) ? ((c + 1) < 16 ? (c + 1) / 4 : 4) : -1;
-    if (next_blk != blk) {                       // block ends here: fold it in
-      if (blk < 4) {
-        const f32x4 scl{sc_tile[(kt * 16 + 4 * g16 + 0) * 4 + blk], sc_tile[(kt * 16 + 4 * g16 + 1) * 4 + blk],
-                        sc_tile[(kt * 16 + 4 * g16 + 2) * 4 + blk], sc_tile[(kt * 16 + 4 * g16 + 3) * 4 + blk]};
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sk[ht][j] = fmaf(tmp[ht][j], scl[j], sk[ht][j]);
-      } else {
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) sk[ht] += tmp[ht];
-      }
-      tmp[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      tmp[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds + 16 l (lds is wave-uniform, passed in M0).  Written as inline asm so that the
+// compiler does not see an LDS write of unknown address in flight: it would otherwise wait
+// for every outstanding transfer before the next LDS read, which defeats the prefetch.
+// Completion is tracked explicitly with wait_vmcnt<> followed by a work-group barrier.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
-// O^T[256 dh .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.
+// LDS layout of one work-group (bytes).  The gather ring holds NBLK 1-KB blocks per tile
+// (one transfer instruction each); instructions past the tile write a junk block.
+template <int ROPE>
+struct MlaGeom {
+  static constexpr int NCH = ROPE ? 41 : 33;            // 16-byte chunks read per row
+  static constexpr int RAW = kTK * NCH;                 // chunks per tile
+  static constexpr int NBLK = (RAW + kWave - 1) / kWave;
+  static constexpr int PER_WAVE = (NBLK + kMlaWaves - 1) / kMlaWaves;
+  static constexpr int STAGE = NBLK * 1024;
+  static constexpr int OFF_JUNK = kNStage * STAGE;
+  static constexpr int OFF_KS = OFF_JUNK + 1024;                      // [kTK][kKS] fp16
+  static constexpr int OFF_SC = OFF_KS + kTK * kKS * 2;               // [4][kTK] f32
+  static constexpr int OFF_MASK = OFF_SC + 4 * kTK * 4;               // [kTK] f32: 0 / -inf
+  static constexpr int OFF_XS = OFF_MASK + kTK * 4;                   // [8][4][64] f32x4
+  static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] fp16
+  static constexpr int OFF_SLOT = OFF_QR + (ROPE ? kHeadsPerWg * kQRS * 2 : 0);
+  static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
+};
+static_assert(MlaGeom<64>::BYTES <= 160 * 1024, "LDS budget");
+
+// Work split inside a work-group of 8 waves (one query row, up to 128 heads): wave w owns
+// head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half dh = w >> 2
+// (latent dims 256 dh .. 256 dh + 255, RoPE dims 32 dh .. 32 dh + 31).  Every K or V
+// fragment read from LDS feeds two MFMAs.  Per wave the latent query takes 64 registers and
+// the output accumulator 128; the RoPE query is read from LDS per tile.
+
+// Partial S^T of key sub-tile kt over this wave's dims: rows = keys 16 kt + 4 g + j, columns
+// = heads.  The two latent blocks are accumulated apart and scaled by their key's scale;
+// loads run two fragments ahead of the MFMAs.
+template <int ROPE, int DH>
+__device__ __forceinline__ void qk_part(const _Float16* ks_tile, const float* sc_tile,
+                                        const _Float16* qr_lane, const f16x8 (&qb)[2][8],
+                                        int kt, f32x4 (&sk)[2], int g16, int c16) {
+  const _Float16* krow = ks_tile + (kt * 16 + c16) * kKS + 256 * DH + 8 * g16;
+  f32x4 t0[2], t1[2], tr[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    t0[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    t1[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tr[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f16x8 ka[2];
+  ka[0] = *reinterpret_cast<const f16x8*>(krow);
+  ka[1] = *reinterpret_cast<const f16x8*>(krow + 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const f16x8 k = ka[i & 1];
+    if (i + 2 < 8) ka[i & 1] = *reinterpret_cast<const f16x8*>(krow + 32 * (i + 2));
+    if (i < 4) {
+      t0[0] = mfma_f16(k, qb[0][i], t0[0]);
+      t0[1] = mfma_f16(k, qb[1][i], t0[1]);
+    } else {
+      t1[0] = mfma_f16(k, qb[0][i], t1[0]);
+      t1[1] = mfma_f16(k, qb[1][i], t1[1]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (ROPE) {
+    const f16x8 kr = *reinterpret_cast<const f16x8*>(ks_tile + (kt * 16 + c16) * kKS + 512 +
+                                                     32 * DH + 8 * g16);
+    const f16x8 q0 = *reinterpret_cast<const f16x8*>(qr_lane);
+    const f16x8 q1 = *reinterpret_cast<const f16x8*>(qr_lane + 16 * kQRS);
+    tr[0] = mfma_f16(kr, q0, tr[0]);
+    tr[1] = mfma_f16(kr, q1, tr[1]);
+  }
+  const f32x4 sa = *reinterpret_cast<const f32x4*>(sc_tile + (2 * DH) * kTK + kt * 16 + 4 * g16);
+  const f32x4 sb = *reinterpret_cast<const f32x4*>(sc_tile + (2 * DH + 1) * kTK + kt * 16 + 4 * g16);
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sk[ht][j] = fmaf(t1[ht][j], sb[j], fmaf(t0[ht][j], sa[j], tr[ht][j]));
+}
+
+// O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.
 template <int DH>
-__device__ __forceinline__ void pv_half(const _Float16* ks_tile, const float* sc_tile,
+__device__ __forceinline__ void pv_part(const _Float16* ks_tile, const float* sc_tile,
                                         const float (&pv)[2][2][4], f32x4 (&o_acc)[2][16],
                                         int g16, int c16) {
+  // lane (g, i) supplies keys {4g + i/4} x dims {16 dt + 4 (i%4) .. +3}; receives dim
+  // 16 dt + i of keys 4g .. 4g+3 (lo) and 16 + 4g .. 16 + 4g + 3 (hi).
+  const _Float16* vbase = ks_tile + (4 * g16 + (c16 >> 2)) * kKS + 256 * DH + 4 * (c16 & 3);
 #pragma unroll
   for (int b2 = 0; b2 < 2; ++b2) {
     const int blk = 2 * DH + b2;
-    float vsc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vsc[e] = sc_tile[((e >> 2) * 16 + 4 * g16 + (e & 3)) * 4 + blk];
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc_tile + blk * kTK + 4 * g16);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc_tile + blk * kTK + 16 + 4 * g16);
     f16x8 pb[2];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
+      for (int j = 0; j < 4; ++j) {
+        pb[ht][j] = (_Float16)(pv[ht][0][j] * v0[j]);
+        pb[ht][4 + j] = (_Float16)(pv[ht][1][j] * v1[j]);
+      }
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-      const int dt = blk * 8 + dd;          // global 16-dim tile
-      // lane (g, i) supplies keys {4g + i/4} x dims {16 dt + 4 (i%4) .. +3}; receives dim
-      // 16 dt + i of keys 4g .. 4g+3 (then 16 + 4g .. 16 + 4g + 3).
-      const _Float16* src0 = ks_tile + (4 * g16 + (c16 >> 2)) * kKS + 16 * dt + 4 * (c16 & 3);
+      __builtin_amdgcn_sched_barrier(0);
+      const _Float16* src0 = vbase + 16 * (b2 * 8 + dd);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0)));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -147,27 +188,25 @@ __device__ __forceinline__ void pv_half(const _Float16* ks_tile, const float* sc
 template <int ROPE>
 __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit,
                                                          int keys_per_split, float* part) {
+  using G = MlaGeom<ROPE>;
   constexpr int NT = kMlaThreads;
-  constexpr int NCH = ROPE ? 41 : 33;            // 16-byte chunks read per row (NoPE: no RoPE)
-  constexpr int NH = (512 + ROPE) / 64;          // 32-wide K chunks per dim half
-  constexpr int RAW = kTK * NCH;                 // chunks per tile
-  constexpr int PER_WAVE = (RAW + NT - 1) / NT;
-  constexpr int STAGE_CHUNKS = PER_WAVE * NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* raw = smem;                                          // [kNStage][STAGE_CHUNKS][16]
-  _Float16* ks_tile = reinterpret_cast<_Float16*>(raw + kNStage * STAGE_CHUNKS * 16);  // [kTK][kKS]
-  float* sc_tile = reinterpret_cast<float*>(ks_tile + kTK * kKS);                      // [kTK][4]
-  float* xs = sc_tile + kTK * 4;                                                       // [8][16][64]
-  int* ok_tile = reinterpret_cast<int*>(xs + kMlaWaves * 16 * kWave);                  // [kTK]
-  int* slot_sh = ok_tile + kTK;                                                        // [keys]
+  _Float16* ks_tile = reinterpret_cast<_Float16*>(smem + G::OFF_KS);
+  float* sc_tile = reinterpret_cast<float*>(smem + G::OFF_SC);
+  float* mask_tile = reinterpret_cast<float*>(smem + G::OFF_MASK);
+  f32x4* xs = reinterpret_cast<f32x4*>(smem + G::OFF_XS);
+  _Float16* qr_sh = reinterpret_cast<_Float16*>(smem + G::OFF_QR);
+  int* slot_sh = reinterpret_cast<int*>(smem + G::OFF_SLOT);
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
+  const int lane0 = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int g16 = lane >> 4, c16 = lane & 15;
   const int hg = wave & 3, dh = wave >> 2;
   const int r = blockIdx.x;
-  const int h0 = blockIdx.y * kHeadsPerWg + hg * 32;
+  const int hbase = blockIdx.y * kHeadsPerWg;
+  const int h0 = hbase + hg * 32;
   const int split = blockIdx.z;
   const SeqView& s = a.s;
   const int H = a.n_heads;
@@ -208,41 +247,66 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     }
     slot_sh[i] = slot;
   }
+  // RoPE query of the group's heads, as fp16, into LDS.
+  if (ROPE) {
+    bool ok = true;
+    for (int i = tid; i < kHeadsPerWg * 8; i += NT) {
+      const int hh = i >> 3, q8 = i & 7;
+      f16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
+      if (hbase + hh < H) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(
+            static_cast<const __bf16*>(a.q) + ((size_t)r * H + hbase + hh) * 576 + 512 + 8 * q8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)x[e];
+          ok &= fabsf(f) <= kF16Max;
+          v[e] = (_Float16)f;
+        }
+      }
+      *reinterpret_cast<f16x8*>(qr_sh + hh * kQRS + 8 * q8) = v;
+    }
+    if (!ok) raise_fault(a.fault, kFaultRange);
+  }
   __syncthreads();
 
-  // Gather: instruction m of a tile moves chunks 64m .. 64m+63 of the tile's rows straight
-  // into LDS (chunk f = key f / NCH, bytes 16 (f % NCH) of its row); lanes past the tile or
-  // on a masked key read the pool's first chunk instead, which staging ignores.
+  // Gather: instruction m of a tile moves chunks 64m .. 64m+63 of the tile's rows into LDS
+  // block m (chunk f = key f / NCH, bytes 16 (f % NCH) of its row); lanes past the tile or
+  // on a masked key read the pool's first chunk instead, which staging ignores.  Every wave
+  // issues exactly PER_WAVE transfers per tile, which the vmcnt waits below rely on.
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
-  auto issue = [&](int tile) {
-    unsigned char* dst = raw + (tile % kNStage) * STAGE_CHUNKS * 16;
+  auto issue = [&](int tile, int lane) {
+    const uint32_t stage = lds0 + (uint32_t)((tile % kNStage) * G::STAGE);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int m = wave + u * kMlaWaves;
+    for (int u = 0; u < G::PER_WAVE; ++u) {
+      const int m = wv + u * kMlaWaves;
       const int f = m * kWave + lane;
       const uint8_t* src = pool;
-      if (f < RAW) {
-        const int kk = f / NCH, j = f - (f / NCH) * NCH;
+      if (f < G::RAW) {
+        const int kk = f / G::NCH, j = f - (f / G::NCH) * G::NCH;
         const int slot = slot_sh[tile * kTK + kk];
         if (slot >= 0) src = pool + (int64_t)slot * kLatRow + 16 * j;
       }
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(dst + (size_t)m * kWave * 16), 16, 0, 0);
+      const uint32_t dst = m < G::NBLK ? stage + (uint32_t)(m * 1024) : lds0 + G::OFF_JUNK;
+      dma16(src, dst);
     }
   };
 
-  // Query fragments for this wave's 32 heads and dim half (B operand of S^T = K Q^T).
+  // Latent query fragments for this wave's 32 heads and dim half (B operand of S^T = K Q^T).
+  const int g16 = lane0 >> 4, c16 = lane0 & 15;
   const bool ht_live[2] = {h0 < H, h0 + 16 < H};
   const bool active = ht_live[0];
-  f16x8 qb[2][NH];
+  f16x8 qb[2][8];
   bool q_range = true;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int hq = ht_live[ht] ? h0 + 16 * ht + c16 : c16;
     const __bf16* qh = static_cast<const __bf16*>(a.q) + ((size_t)r * H + hq) * (512 + ROPE) +
-                       8 * g16 + 32 * NH * dh;
+                       256 * dh + 8 * g16;
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * i);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -252,7 +316,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       }
     }
   }
-  if (__any(!q_range) && active && lane == 0) raise_fault(a.fault, kFaultRange);
+  if (__any(!q_range) && active && lane0 == 0) raise_fault(a.fault, kFaultRange);
   const float qk_scale = a.softmax_scale * ssmax_mult(a.ssmax_s, row_ok ? p : 0) * kLog2e;
 
   f32x4 o_acc[2][16];
@@ -263,21 +327,28 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
   float l_part[2] = {0.f, 0.f};
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  if (ntiles > 0) issue(0, lane0);
+  if (ntiles > 1) issue(1, lane0);
   for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 2 < ntiles) issue(tile + 2);
+    // Lane-derived addresses are recomputed every tile (a few VALU instructions) rather than
+    // hoisted out of the loop: the query and the accumulator leave no registers to keep them.
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int g16 = lane >> 4, c16 = lane & 15;
+    const _Float16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
+    if (tile + 2 < ntiles) issue(tile + 2, lane);
     const int ahead = min(2, ntiles - 1 - tile);
-    if (ahead == 2) wait_vmcnt<2 * PER_WAVE>();
-    else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+    if (ahead == 2) wait_vmcnt<2 * G::PER_WAVE>();
+    else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
     else wait_vmcnt<0>();
-    __syncthreads();   // every wave's chunks of this tile are in LDS; last tile's math done
+    __syncthreads();   // every wave's transfers of this tile landed; last tile's math done
 
-    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key flags
+    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key masks
     {
-      const unsigned char* src = raw + (tile % kNStage) * STAGE_CHUNKS * 16;
-      for (int f = tid; f < RAW; f += NT) {
-        const int kk = f / NCH, j = f - (f / NCH) * NCH;
+      const unsigned char* src = smem + (tile % kNStage) * G::STAGE;
+      bool in_range = true;
+      for (int f = tid; f < G::RAW; f += NT) {
+        const int kk = f / G::NCH, j = f - (f / G::NCH) * G::NCH;
         const bool ok = slot_sh[tile * kTK + kk] >= 0;
         const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * f) : u32x4{0, 0, 0, 0};
         if (j < 32) {
@@ -288,64 +359,69 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
             *reinterpret_cast<f16x8*>(kd + 8 * h) =
                 f16x8{f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
           }
-          if (j == 0) ok_tile[kk] = ok;
+          if (j == 0) mask_tile[kk] = ok ? 0.f : -__builtin_inff();
         } else if (j == 32) {
-          *reinterpret_cast<u32x4*>(sc_tile + kk * 4) = v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sc = __uint_as_float(v[e]);
+            in_range &= !ok || (fabsf(sc) <= kMaxVScale);
+            sc_tile[e * kTK + kk] = sc;
+          }
         } else {
           const bf16x8 rb = __builtin_bit_cast(bf16x8, v);
           f16x8 rh;
-          bool in_range = true;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float f2 = (float)rb[e];
             in_range &= fabsf(f2) <= kF16Max;
             rh[e] = (_Float16)f2;
           }
-          if (!in_range) raise_fault(a.fault, kFaultRange);
           *reinterpret_cast<f16x8*>(ks_tile + kk * kKS + 512 + 8 * (j - 33)) = rh;
         }
       }
+      if (!in_range) raise_fault(a.fault, kFaultRange);
     }
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- partial S^T over this wave's dim half per key sub-tile, exchanged through LDS;
-    //      both partner waves then add half 0 + half 1 in the same order
+    // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
+    //      partner waves then add half 0 + half 1 in the same order
     {
-      f32x4* mine = reinterpret_cast<f32x4*>(xs + wave * 16 * kWave);
+      f32x4* mine = xs + wave * 4 * kWave;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 sk[2];
-        if (dh == 0) qk_half<ROPE, 0>(ks_tile, sc_tile, qb, kt, sk, g16, c16);
-        else qk_half<ROPE, 1>(ks_tile, sc_tile, qb, kt, sk, g16, c16);
+        if (dh == 0) qk_part<ROPE, 0>(ks_tile, sc_tile, qr_lane, qb, kt, sk, g16, c16);
+        else qk_part<ROPE, 1>(ks_tile, sc_tile, qr_lane, qb, kt, sk, g16, c16);
         mine[(2 * kt) * kWave + lane] = sk[0];
         mine[(2 * kt + 1) * kWave + lane] = sk[1];
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
-    f32x4 sacc[2][2];
+    float pv[2][2][4];
     {
-      const f32x4* h0p = reinterpret_cast<const f32x4*>(xs + (wave & 3) * 16 * kWave);
-      const f32x4* h1p = reinterpret_cast<const f32x4*>(xs + ((wave & 3) | 4) * 16 * kWave);
+      const f32x4* p0 = xs + hg * 4 * kWave;
+      const f32x4* p1 = xs + (hg | 4) * 4 * kWave;
+      const f32x4 mk0 = *reinterpret_cast<const f32x4*>(mask_tile + 4 * g16);
+      const f32x4 mk1 = *reinterpret_cast<const f32x4*>(mask_tile + 16 + 4 * g16);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) sacc[q4 >> 1][q4 & 1] = h0p[q4 * kWave + lane] + h1p[q4 * kWave + lane];
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const f32x4 sum = p0[(2 * kt + ht) * kWave + lane] + p1[(2 * kt + ht) * kWave + lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pv[ht][kt][j] = fmaf(sum[j], qk_scale, kt ? mk1[j] : mk0[j]);
+        }
     }
 
     // ---- online softmax (base 2) per head (lane column), identical in both partner waves
-    float pv[2][2][4];
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       float mt = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = ok_tile[kt * 16 + 4 * g16 + j] ? sacc[kt][ht][j] * qk_scale
-                                                         : -__builtin_inff();
-          pv[ht][kt][j] = v;
-          mt = fmaxf(mt, v);
-        }
+        for (int j = 0; j < 4; ++j) mt = fmaxf(mt, pv[ht][kt][j]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const bool need = mt > m_run[ht] + kRescaleSlack || (m_run[ht] == -__builtin_inff() && mt > m_run[ht]);
@@ -357,11 +433,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         for (int i = 0; i < 16; ++i) o_acc[ht][i] *= alpha;
         m_run[ht] = m_new;
       }
+      // With no finite logit yet every value is -inf and exp2(-inf - 0) = 0.
+      const float msub = (m_run[ht] == -__builtin_inff()) ? 0.f : m_run[ht];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float e = (m_run[ht] == -__builtin_inff()) ? 0.f : exp2f(pv[ht][kt][j] - m_run[ht]);
+          const float e = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub);
           pv[ht][kt][j] = e;
           l_part[ht] += e;
         }
@@ -369,8 +447,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T over this wave's dim half
-    if (dh == 0) pv_half<0>(ks_tile, sc_tile, pv, o_acc, g16, c16);
-    else pv_half<1>(ks_tile, sc_tile, pv, o_acc, g16, c16);
+    if (dh == 0) pv_part<0>(ks_tile, sc_tile, pv, o_acc, g16, c16);
+    else pv_part<1>(ks_tile, sc_tile, pv, o_acc, g16, c16);
   }
 
   // ---- epilogue: lane (g, i) holds O[head h0 + 16 ht + i][dims 256 dh + 16 t + 4 g + j]
@@ -408,11 +486,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 
 template <int ROPE>
 constexpr size_t mla_lds_bytes() {
-  constexpr int NCH = ROPE ? 41 : 33;
-  constexpr int RAW = kTK * NCH;
-  constexpr int PER_WAVE = (RAW + kMlaThreads - 1) / kMlaThreads;
-  return (size_t)kNStage * PER_WAVE * kMlaThreads * 16 + (size_t)kTK * kKS * 2 + kTK * 4 * 4 +
-         kMlaWaves * 16 * kWave * 4 + kTK * 4 + kMaxSplitKeys * 4;
+  return (size_t)MlaGeom<ROPE>::BYTES;
 }
 
 // Merge split partials: o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) (base-2 lse).
