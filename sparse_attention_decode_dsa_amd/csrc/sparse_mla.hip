@@ -50,6 +50,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) short lds_short;
 
 constexpr int kNStage = 3;         // gather ring: the tile being staged + two in flight
+
+// Source of the gather for masked keys and for lanes past the end of a tile.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 constexpr float kF16Max = 65504.0f;
 constexpr int kMaxSplitKeys = 2048;   // top_k <= 2048
 constexpr int kMlaThreads = 512;
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, tid0 = tid;
   const int lane0 = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int hg = wave & 3, dh = wave >> 2;
@@ -273,8 +276,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 
   // Gather: instruction m of a tile moves chunks 64m .. 64m+63 of the tile's rows into LDS
   // block m (chunk f = key f / NCH, bytes 16 (f % NCH) of its row); lanes past the tile or
-  // on a masked key read the pool's first chunk instead, which staging ignores.  Every wave
-  // issues exactly PER_WAVE transfers per tile, which the vmcnt waits below rely on.
+  // on a masked key read zeros instead.  Every wave issues exactly PER_WAVE transfers per
+  // tile, which the vmcnt waits below rely on.
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
   auto issue = [&](int tile, int lane) {
     const uint32_t stage = lds0 + (uint32_t)((tile % kNStage) * G::STAGE);
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     for (int u = 0; u < G::PER_WAVE; ++u) {
       const int m = wv + u * kMlaWaves;
       const int f = m * kWave + lane;
-      const uint8_t* src = pool;
+      const uint8_t* src = g_zero_row;
       if (f < G::RAW) {
         const int kk = f / G::NCH, j = f - (f / G::NCH) * G::NCH;
         const int slot = slot_sh[tile * kTK + kk];
@@ -343,32 +346,49 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     else wait_vmcnt<0>();
     __syncthreads();   // every wave's transfers of this tile landed; last tile's math done
 
-    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key masks
+    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key masks.  Masked
+    //      keys were gathered from a zero row, so no per-chunk check is needed.  Each thread
+    //      converts two 16-byte latent chunks and at most one scale / RoPE chunk; all LDS
+    //      reads are issued before the conversions.
     {
+      constexpr int NX = G::NCH - 32;                // scale + RoPE chunks per key
       const unsigned char* src = smem + (tile % kNStage) * G::STAGE;
-      bool in_range = true;
-      for (int f = tid; f < G::RAW; f += NT) {
-        const int kk = f / G::NCH, j = f - (f / G::NCH) * G::NCH;
-        const bool ok = slot_sh[tile * kTK + kk] >= 0;
-        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * f) : u32x4{0, 0, 0, 0};
-        if (j < 32) {
-          _Float16* kd = ks_tile + kk * kKS + 16 * j;
+      int tid = tid0;
+      asm volatile("" : "+v"(tid));                  // recomputed per tile, not hoisted
+      u32x4 v[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const f16x4 f0 = e4m3x4_to_f16(v[2 * h]), f1 = e4m3x4_to_f16(v[2 * h + 1]);
-            *reinterpret_cast<f16x8*>(kd + 8 * h) =
-                f16x8{f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-          }
-          if (j == 0) mask_tile[kk] = ok ? 0.f : -__builtin_inff();
-        } else if (j == 32) {
+      for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;                  // latent chunk i: key i >> 5, chunk i & 31
+        v[u] = *reinterpret_cast<const u32x4*>(src + 16 * ((i >> 5) * G::NCH + (i & 31)));
+      }
+      const bool has_x = tid < kTK * NX;
+      const int xk = tid / NX, xj = tid - (tid / NX) * NX;
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (has_x) w = *reinterpret_cast<const u32x4*>(src + 16 * (xk * G::NCH + 32 + xj));
+      int slot = 0;
+      if (tid < kTK) slot = slot_sh[tile * kTK + tid];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;
+        _Float16* kd = ks_tile + (i >> 5) * kKS + 16 * (i & 31);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f16x4 f0 = e4m3x4_to_f16(v[u][2 * h]), f1 = e4m3x4_to_f16(v[u][2 * h + 1]);
+          *reinterpret_cast<f16x8*>(kd + 8 * h) =
+              f16x8{f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+        }
+      }
+      if (has_x) {
+        bool in_range = true;
+        if (xj == 0) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float sc = __uint_as_float(v[e]);
-            in_range &= !ok || (fabsf(sc) <= kMaxVScale);
-            sc_tile[e * kTK + kk] = sc;
+            const float sc = __uint_as_float(w[e]);
+            in_range &= fabsf(sc) <= kMaxVScale;
+            sc_tile[e * kTK + xk] = sc;
           }
         } else {
-          const bf16x8 rb = __builtin_bit_cast(bf16x8, v);
+          const bf16x8 rb = __builtin_bit_cast(bf16x8, w);
           f16x8 rh;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -376,10 +396,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
             in_range &= fabsf(f2) <= kF16Max;
             rh[e] = (_Float16)f2;
           }
-          *reinterpret_cast<f16x8*>(ks_tile + kk * kKS + 512 + 8 * (j - 33)) = rh;
+          *reinterpret_cast<f16x8*>(ks_tile + xk * kKS + 512 + 8 * (xj - 1)) = rh;
         }
+        if (!in_range) raise_fault(a.fault, kFaultRange);
       }
-      if (!in_range) raise_fault(a.fault, kFaultRange);
+      if (tid < kTK) mask_tile[tid] = slot >= 0 ? 0.f : -__builtin_inff();
     }
     __syncthreads();
 
