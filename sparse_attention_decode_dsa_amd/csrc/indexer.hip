@@ -34,6 +34,22 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kKeyStride = 136;   // fp16 per key row in LDS (128 + 8): conflict-free b128 reads
 
+// v[s] summed over the four 16-lane groups, delivered to lane group s (same column):
+// permlane32_swap pairs groups g and g ^ 2, permlane16_swap then pairs g and g ^ 1.
+__device__ __forceinline__ float sum_over_lane_groups(const float (&v)[4]) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]),
+                                                  false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]),
+                                                  false, false);
+  const float xs = __uint_as_float(x[0]) + __uint_as_float(x[1]);   // groups 0,1: v0; 2,3: v2
+  const float ys = __uint_as_float(y[0]) + __uint_as_float(y[1]);   // groups 0,1: v1; 2,3: v3
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(xs), __float_as_uint(ys),
+                                                  false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+constexpr int kMaxKeysPerWg = 4096;
+
 // R = query rows per work-group (1, 2 or 4), HT = 16-head tiles (n_heads / 16).
 template <int R, int HT>
 __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int groups_per_seq,
@@ -41,6 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
   __shared__ __attribute__((aligned(16))) _Float16 ktile[2][kStepKeys * kKeyStride];
   __shared__ float kscale[2][kStepKeys];
   __shared__ int kok[2][kStepKeys / 16];
+  __shared__ int blk_sh[kMaxKeysPerWg / 16];   // block of each 16-key group of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -79,6 +96,20 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
   constexpr int kSubPerWave = R;
   const int sub0 = wave / R;
 
+  const int32_t* bt = s.block_table + (size_t)b * s.mbps;
+  const int k_end = min(k_hi, pmax + 1);          // keys scored: k_lo .. k_end - 1
+  // Block of every 16-key group up to k_end (16 consecutive keys share a block since the
+  // block size is a power of two >= 16); -1 marks a block id outside the pool.
+  for (int gi = tid; gi * 16 < k_end - k_lo; gi += kThreads) {
+    const int blk = bt[(k_lo + 16 * gi) >> s.lbs];
+    if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
+      raise_fault(a.fault, 1u << 0);
+      blk_sh[gi] = -1;
+    } else {
+      blk_sh[gi] = blk;
+    }
+  }
+
   // Query fragments (A operand: head on M, dims on K).  Lane group g holds dims 32g .. 32g+31
   // as four K=32 chunks; the key side uses the same split, so the dims pair up.
   f16x8 qa[HT][4];
@@ -104,40 +135,46 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
   }
   const float mrow = ssmax_mult(a.ssmax_s, max(pos, 0));
 
-  const int32_t* bt = s.block_table + (size_t)b * s.mbps;
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
   const int bs_mask = (1 << s.lbs) - 1;
   const float ninf = -__builtin_inff();
 
-  // Staging: thread -> (key kk = tid / 4, quarter qq = tid % 4) of a 64-key step.
+  // Keys past every row's position only get -inf.
+  for (int t = max(k_lo, k_end) + tid; t < k_hi; t += kThreads)
+    for (int j = 0; j < nrows; ++j) a.scores[(size_t)(row0 + j) * a.ld + t] = ninf;
+  const int nsteps = (k_end - k_lo + kStepKeys - 1) / kStepKeys;
+  if (nsteps <= 0) return;
+  __syncthreads();   // blk_sh
+
+  // Staging: thread -> (key kk = tid / 4, quarter qq = tid % 4) of a 64-key step.  Two
+  // register sets keep the loads of two steps in flight.
   const int kk = tid >> 2, qq = tid & 3;
-  u32x4 st_lo, st_hi;
-  float st_scale;
-  int st_ok;
-  auto load_step = [&](int t0) {
-    st_lo = u32x4{0, 0, 0, 0};
-    st_hi = u32x4{0, 0, 0, 0};
-    st_scale = 0.f;
-    st_ok = 0;
+  struct Stage {
+    u32x4 lo, hi;
+    float scale;
+    int ok;
+  };
+  auto load_step = [&](Stage& S, int t0) {
+    S.lo = u32x4{0, 0, 0, 0};
+    S.hi = u32x4{0, 0, 0, 0};
+    S.scale = 0.f;
+    S.ok = 0;
     const int t = t0 + kk;
-    if (t > pmax || t >= k_hi) return;      // past every row: no block of the table is read
-    const int blk = bt[t >> s.lbs];   // 16 consecutive keys share a block (bs >= 16)
-    if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
-      if (qq == 0 && (kk & 15) == 0) raise_fault(a.fault, 1u << 0);
-      return;
-    }
+    if (t >= k_end) return;      // past every row: nothing is read
+    const int blk = blk_sh[(t - k_lo) >> 4];
+    if (blk < 0) return;
     const uint8_t* rp = pool + (((int64_t)blk << s.lbs) + (t & bs_mask)) * kIdxRow;
     const u32x4a4 v0 = *reinterpret_cast<const u32x4a4*>(rp + 32 * qq);
     const u32x4a4 v1 = *reinterpret_cast<const u32x4a4*>(rp + 32 * qq + 16);
-    st_lo = u32x4{v0[0], v0[1], v0[2], v0[3]};
-    st_hi = u32x4{v1[0], v1[1], v1[2], v1[3]};
-    if (qq == 0) st_scale = *reinterpret_cast<const float*>(rp + 128);
-    st_ok = 1;
+    S.lo = u32x4{v0[0], v0[1], v0[2], v0[3]};
+    S.hi = u32x4{v1[0], v1[1], v1[2], v1[3]};
+    if (qq == 0) S.scale = *reinterpret_cast<const float*>(rp + 128);
+    S.ok = 1;
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](const Stage& S, int buf) {
     _Float16* dst = &ktile[buf][kk * kKeyStride + 32 * qq];
-    const uint32_t w8[8] = {st_lo[0], st_lo[1], st_lo[2], st_lo[3],
-                            st_hi[0], st_hi[1], st_hi[2], st_hi[3]};
+    const uint32_t w8[8] = {S.lo[0], S.lo[1], S.lo[2], S.lo[3],
+                            S.hi[0], S.hi[1], S.hi[2], S.hi[3]};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const f16x4 lo = e4m3x4_to_f16(w8[2 * c]);
@@ -145,55 +182,61 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
       *reinterpret_cast<f16x8*>(dst + 8 * c) =
           f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    if (qq == 0) kscale[buf][kk] = st_scale;
-    if (qq == 0 && (kk & 15) == 0) kok[buf][kk >> 4] = st_ok;
+    if (qq == 0) kscale[buf][kk] = S.scale;
+    if (qq == 0 && (kk & 15) == 0) kok[buf][kk >> 4] = S.ok;
   };
-
-  const int nsteps = (min(k_hi, pmax + 1) - k_lo + kStepKeys - 1) / kStepKeys;
-  // Keys past every row's position only get -inf.
-  for (int t = max(k_lo, pmax + 1) + tid; t < k_hi; t += kThreads)
-    for (int j = 0; j < nrows; ++j) a.scores[(size_t)(row0 + j) * a.ld + t] = ninf;
-  if (nsteps <= 0) return;
-
-  load_step(k_lo);
-  store_step(0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
+  // Scores of one 64-key step for this wave's row.  Each lane accumulates, per sub-tile, the
+  // weighted ReLU over the 4 heads of each head tile it holds; one cross-lane transpose-sum
+  // (two permlane32 and one permlane16 swap) then leaves sub-tile g's totals in lane group g,
+  // so the row's results leave in one store per step.  K fragments of the next sub-tile are
+  // read while the current one multiplies.
+  auto compute_step = [&](int st, int buf) {
     const int t0 = k_lo + st * kStepKeys;
-    const int buf = st & 1;
-    if (st + 1 < nsteps) load_step(t0 + kStepKeys);   // in flight during this step
-
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    f16x8 kb[2][4];
+    auto read_frags = [&](f16x8 (&dst)[4], int sub) {
+      const _Float16* krow = &ktile[buf][(16 * sub + c16) * kKeyStride + 32 * g16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c] = *reinterpret_cast<const f16x8*>(krow + 8 * c);
+    };
+    read_frags(kb[0], sub0);
 #pragma unroll
     for (int si = 0; si < kSubPerWave; ++si) {
-      const int sub = sub0 + si * (kWaves / R);
-      const int tk = t0 + 16 * sub;
-      if (tk >= k_hi) continue;
-      const int t = tk + c16;
-      float part = 0.f;
-      const bool ok = kok[buf][sub] != 0;
-      if (ok) {
-        const _Float16* krow = &ktile[buf][(16 * sub + c16) * kKeyStride + 32 * g16];
-        f16x8 kb[4];
+      if (si + 1 < kSubPerWave) read_frags(kb[(si + 1) & 1], sub0 + (si + 1) * (kWaves / R));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const f16x8*>(krow + 8 * c);
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4 d{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          f32x4 d{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 4; ++c) d = mfma_f16(qa[ht][c], kb[si & 1][c], d);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) d = mfma_f16(qa[ht][c], kb[c], d);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wq[ht][i], relu_bits(d[i]), part);
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
+        for (int i = 0; i < 4; ++i) part[si] = fmaf(wq[ht][i], relu_bits(d[i]), part[si]);
       }
-      if (row_live && lane < 16 && t < k_hi)
-        a.scores[(size_t)row * a.ld + t] =
-            (ok && t <= pos) ? part * kscale[buf][16 * sub + c16] * mrow : ninf;
     }
-    if (st + 1 < nsteps) {
-      store_step(buf ^ 1);   // the other buffer was last read two steps ago
+    const float tot = sum_over_lane_groups(part);
+    const int sub = sub0 + g16 * (kWaves / R);     // this lane group's sub-tile
+    const int t = t0 + 16 * sub + c16;
+    if (row_live && g16 < kSubPerWave && t < k_hi) {
+      const bool ok = t < k_end && t <= pos && kok[buf][sub] != 0;
+      a.scores[(size_t)row * a.ld + t] = ok ? tot * kscale[buf][16 * sub + c16] * mrow : ninf;
     }
+  };
+
+  Stage SA, SB;
+  load_step(SA, k_lo);
+  if (nsteps > 1) load_step(SB, k_lo + kStepKeys);
+  store_step(SA, 0);
+  __syncthreads();
+  // Step st computes buffer st & 1, issues the loads of step st + 2 and stages step st + 1
+  // (loaded during step st - 1) into the other buffer.
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 2 < nsteps) load_step(SA, k_lo + (st + 2) * kStepKeys);
+    compute_step(st, 0);
+    if (st + 1 < nsteps) store_step(SB, 1);
+    __syncthreads();
+    if (st + 1 >= nsteps) break;
+    if (st + 3 < nsteps) load_step(SB, k_lo + (st + 3) * kStepKeys);
+    compute_step(st + 1, 1);
+    if (st + 2 < nsteps) store_step(SA, 0);
     __syncthreads();
   }
 }
@@ -274,7 +317,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
   const long long groups = (long long)s.batch * gps;
   // Keys per work-group: long chunks amortise loading the queries; shrink them until the
   // grid covers the 256 CUs several times over.
-  int kpw = 4096;
+  int kpw = kMaxKeysPerWg;
   while (kpw > 256 && groups * ((s.max_seq_len + kpw - 1) / kpw) < 2048) kpw >>= 1;
   dim3 grid((s.max_seq_len + kpw - 1) / kpw, (unsigned)groups);
   switch (R) {
