@@ -76,10 +76,10 @@ enum ml4_fault_bits {
   ML4_FAULT_TOPK_INDEX = 1u << 1,  /* topk entry outside [0, q_pos] or topk_len > top_k    */
   ML4_FAULT_NAN_SCORE = 1u << 2,   /* a candidate score was NaN (ranked below -inf)        */
   ML4_FAULT_QPOS = 1u << 3,        /* q_pos outside [0, seq_len) or > max_seq_len - 1      */
-  ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a bf16 query or RoPE key element beyond the
-                                      fp16 range (|x| > 65504) or NaN, or a selected key's
-                                      latent scale with |s| > 128 or NaN; that row's output
-                                      is unspecified                                       */
+  ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a bf16 latent-query element beyond the fp16
+                                      range (|x| > 65504) or NaN, or a selected key's latent
+                                      scale with |s| > 128 or NaN; that row's output is
+                                      unspecified                                          */
 };
 
 /* A batch of requests.  [host] struct; the arrays are device memory.
@@ -163,10 +163,10 @@ int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, i
  *   out      [total_q][n_heads][512]: bf16 (fp8 cache) or fp32 (fp32 cache).   lse: fp32
  *            [total_q][n_heads] or NULL.
  *   ws       ml4_workspace_bytes(ML4_ENTRY_MLA, ...) bytes (split-K partials; may be 0).
- * Dequantisation of e4m3 codes is exact.  With the fp8 cache QK and PV run on fp16 MFMA with
- * fp32 accumulation: bf16 query and RoPE-key elements are rounded to fp16 (an element
- * beyond the fp16 range raises ML4_FAULT_RANGE), the softmax weights are rounded to fp16
- * after the running-max shift (so they lie in [0, 1]).
+ * Dequantisation of e4m3 codes is exact.  With the fp8 cache the latent QK and PV products
+ * run on fp16 MFMA and the RoPE product on bf16 MFMA, all with fp32 accumulation: the bf16
+ * latent query is rounded to fp16 (an element beyond the fp16 range raises
+ * ML4_FAULT_RANGE), the softmax weights are rounded to fp16 after the running-max shift.
  */
 int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
                           int32_t q_dtype, int32_t n_heads, int32_t rope_dim,

@@ -11,22 +11,24 @@
 // One work-group = one query row x up to 128 heads x a contiguous range of its selected
 // keys, 8 waves.  Per 32-key tile:
 //   gather  the selected 656-byte rows (slot = block_table[t / bs] * bs + t % bs) straight
-//           into an LDS ring with 16-byte global->LDS transfers, two tiles ahead of the math;
-//   stage   decode the e4m3 codes exactly to fp16 into a [key][576] tile (the bf16 RoPE part
-//           is rounded to fp16; a value beyond the fp16 range is reported), keep the four
-//           per-128 scales in fp32 beside it (a NoPE layer never touches the RoPE bytes);
-//   QK      S^T = K . Q^T on v_mfma_f32_16x16x32_f16 with keys on M and heads on N; each wave
+//           into an LDS ring with 16-byte global->LDS transfers, up to three tiles ahead of
+//           the math; the rows keep the cache layout and are never rewritten;
+//   QK      S^T = K . Q^T with keys on M and heads on N.  Latent K fragments are read as
+//           e4m3 and decoded exactly to fp16 in registers for v_mfma_f32_16x16x32_f16 (the
+//           bf16 query is rounded to fp16, a value beyond its range is reported); each wave
 //           contracts one half of the latent dims (its two 128-dim scale blocks, each summed
-//           on its own and multiplied by its key's scale in fp32) plus half of the RoPE dims,
-//           for 32 heads; the partner wave's half arrives through LDS;
+//           on its own and multiplied by its key's scale in fp32) and half of the RoPE dims on
+//           v_mfma_f32_16x16x32_bf16 with both operands exact, for 32 heads; the partner
+//           wave's half arrives through LDS (a NoPE layer never touches the RoPE bytes);
 //   softmax online, base 2, per head = per lane column; the running maximum only moves when
 //           a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled;
 //   PV      O^T = V^T . P^T on v_mfma_f32_16x16x32_f16 with latent columns on M, heads on
-//           N, over the wave's 256 latent dims: V^T fragments come from the fp16 tile through
-//           ds_read_b64_tr_b16, P^T comes from the QK accumulators in place (the key order of
-//           both operands is the same permutation), and the per-128 scale of V is folded into
-//           P per column block.  fp16 keeps 11 significant bits of P, which bounds the output
-//           error by 2^-11 * sum_t p_t |c_t| even when SSMax makes the softmax peaked.
+//           N, over the wave's 256 latent dims: V^T fragments come from the e4m3 rows through
+//           ds_read_b64_tr_b8 and are decoded in registers, P^T comes from the QK
+//           accumulators in place (the key order of both operands is the same permutation),
+//           and the per-128 scale of V is folded into P per column block.  fp16 keeps 11
+//           significant bits of P, which bounds the output error by 2^-11 * sum_t p_t |c_t|
+//           even when SSMax makes the softmax peaked.
 // A row's selected keys may be split across work-groups; the partial results are merged by
 // their log-sum-exp in a second kernel.
 #include "ml4_device.h"
@@ -37,8 +39,7 @@ namespace {
 
 constexpr int kLatRow = 656;
 constexpr int kTK = 32;            // keys per tile
-constexpr int kKS = 584;           // fp16 stride of a key row of the tile (576 + 8)
-constexpr int kQRS = 72;           // fp16 stride of a head's RoPE query in LDS (64 + 8)
+constexpr int kQRS = 72;           // bf16 stride of a head's RoPE query in LDS (64 + 8)
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kMaxVScale = 128.0f;   // 2^8 * 128 * 448 stays inside fp16 after P * scale
 constexpr uint32_t kFaultBlock = 1u << 0;
@@ -46,10 +47,8 @@ constexpr uint32_t kFaultTopk = 1u << 1;
 constexpr uint32_t kFaultQpos = 1u << 3;
 constexpr uint32_t kFaultRange = 1u << 4;
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) short lds_short;
 
-constexpr int kNStage = 3;         // gather ring: the tile being staged + two in flight
+constexpr int kNStage = 4;         // gather ring: the tile being read + up to three in flight
 
 // Source of the gather for masked keys and for lanes past the end of a tile.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
@@ -76,21 +75,40 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// Sum / maximum over the four 16-lane groups, in every lane of a column: permlane32_swap
+// pairs lane groups g and g ^ 2, permlane16_swap then pairs g and g ^ 1.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+}
+__device__ __forceinline__ float sum_over_lane_groups(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
 // LDS layout of one work-group (bytes).  The gather ring holds NBLK 1-KB blocks per tile
-// (one transfer instruction each); instructions past the tile write a junk block.
+// (one transfer instruction each); instructions past the tile write a junk block.  The
+// tile's rows sit at a stride of RS = 16 NCH bytes with the cache row's own layout, and the
+// matrix-core operands are read from there directly.
 template <int ROPE>
 struct MlaGeom {
   static constexpr int NCH = ROPE ? 41 : 33;            // 16-byte chunks read per row
+  static constexpr int RS = 16 * NCH;                   // bytes per gathered row
   static constexpr int RAW = kTK * NCH;                 // chunks per tile
   static constexpr int NBLK = (RAW + kWave - 1) / kWave;
   static constexpr int PER_WAVE = (NBLK + kMlaWaves - 1) / kMlaWaves;
   static constexpr int STAGE = NBLK * 1024;
   static constexpr int OFF_JUNK = kNStage * STAGE;
-  static constexpr int OFF_KS = OFF_JUNK + 1024;                      // [kTK][kKS] fp16
-  static constexpr int OFF_SC = OFF_KS + kTK * kKS * 2;               // [4][kTK] f32
-  static constexpr int OFF_MASK = OFF_SC + 4 * kTK * 4;               // [kTK] f32: 0 / -inf
-  static constexpr int OFF_XS = OFF_MASK + kTK * 4;                   // [8][4][64] f32x4
-  static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] fp16
+  static constexpr int OFF_XS = OFF_JUNK + 1024;                      // [8][4][64] f32x4
+  static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] bf16
   static constexpr int OFF_SLOT = OFF_QR + (ROPE ? kHeadsPerWg * kQRS * 2 : 0);
   static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
 };
@@ -102,14 +120,20 @@ static_assert(MlaGeom<64>::BYTES <= 160 * 1024, "LDS budget");
 // fragment read from LDS feeds two MFMAs.  Per wave the latent query takes 64 registers and
 // the output accumulator 128; the RoPE query is read from LDS per tile.
 
+// Latent bytes of a gathered row: [512 e4m3][4 x fp32 scale][64 x bf16 RoPE].
+constexpr int kScaleOff = 512;
+constexpr int kRopeOff = 528;
+
 // Partial S^T of key sub-tile kt over this wave's dims: rows = keys 16 kt + 4 g + j, columns
-// = heads.  The two latent blocks are accumulated apart and scaled by their key's scale;
-// loads run two fragments ahead of the MFMAs.
+// = heads.  K fragments are read as e4m3 (8 bytes per lane, all eight issued first) and
+// decoded exactly to fp16 in registers; the two latent blocks are accumulated apart and
+// scaled by their key's scale; the RoPE part runs on bf16 MFMA with both operands exact.
 template <int ROPE, int DH>
-__device__ __forceinline__ void qk_part(const _Float16* ks_tile, const float* sc_tile,
-                                        const _Float16* qr_lane, const f16x8 (&qb)[2][8],
-                                        int kt, f32x4 (&sk)[2], int g16, int c16) {
-  const _Float16* krow = ks_tile + (kt * 16 + c16) * kKS + 256 * DH + 8 * g16;
+__device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* qr_lane,
+                                        const f16x8 (&qb)[2][8], int kt, f32x4 (&sk)[2],
+                                        int g16, int c16) {
+  constexpr int RS = MlaGeom<ROPE>::RS;
+  const unsigned char* krow = raw + (kt * 16 + c16) * RS + 256 * DH + 8 * g16;
   f32x4 t0[2], t1[2], tr[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
@@ -117,14 +141,15 @@ __device__ __forceinline__ void qk_part(const _Float16* ks_tile, const float* sc
     t1[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     tr[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  f16x8 ka[2];
-  ka[0] = *reinterpret_cast<const f16x8*>(krow);
-  ka[1] = *reinterpret_cast<const f16x8*>(krow + 32);
+  u32x2 kw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kw[i] = *reinterpret_cast<const u32x2*>(krow + 32 * i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    const f16x8 k = ka[i & 1];
-    if (i + 2 < 8) ka[i & 1] = *reinterpret_cast<const f16x8*>(krow + 32 * (i + 2));
+    const u32x2 w = kw[i];
+    const f16x4 lo = e4m3x4_to_f16(w[0]), hi = e4m3x4_to_f16(w[1]);
+    const f16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     if (i < 4) {
       t0[0] = mfma_f16(k, qb[0][i], t0[0]);
       t0[1] = mfma_f16(k, qb[1][i], t0[1]);
@@ -135,52 +160,69 @@ __device__ __forceinline__ void qk_part(const _Float16* ks_tile, const float* sc
   }
   __builtin_amdgcn_sched_barrier(0);
   if (ROPE) {
-    const f16x8 kr = *reinterpret_cast<const f16x8*>(ks_tile + (kt * 16 + c16) * kKS + 512 +
-                                                     32 * DH + 8 * g16);
-    const f16x8 q0 = *reinterpret_cast<const f16x8*>(qr_lane);
-    const f16x8 q1 = *reinterpret_cast<const f16x8*>(qr_lane + 16 * kQRS);
-    tr[0] = mfma_f16(kr, q0, tr[0]);
-    tr[1] = mfma_f16(kr, q1, tr[1]);
+    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(
+        raw + (kt * 16 + c16) * RS + kRopeOff + 2 * (32 * DH + 8 * g16));
+    const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
+    const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
+    tr[0] = mfma_bf16(kr, q0, tr[0]);
+    tr[1] = mfma_bf16(kr, q1, tr[1]);
   }
-  const f32x4 sa = *reinterpret_cast<const f32x4*>(sc_tile + (2 * DH) * kTK + kt * 16 + 4 * g16);
-  const f32x4 sb = *reinterpret_cast<const f32x4*>(sc_tile + (2 * DH + 1) * kTK + kt * 16 + 4 * g16);
+  f32x2 sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    sc[j] = *reinterpret_cast<const f32x2*>(raw + (kt * 16 + 4 * g16 + j) * RS + kScaleOff +
+                                            8 * DH);
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sk[ht][j] = fmaf(t1[ht][j], sb[j], fmaf(t0[ht][j], sa[j], tr[ht][j]));
+    for (int j = 0; j < 4; ++j)
+      sk[ht][j] = fmaf(t1[ht][j], sc[j][1], fmaf(t0[ht][j], sc[j][0], tr[ht][j]));
 }
 
-// O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.
-template <int DH>
-__device__ __forceinline__ void pv_part(const _Float16* ks_tile, const float* sc_tile,
-                                        const float (&pv)[2][2][4], f32x4 (&o_acc)[2][16],
-                                        int g16, int c16) {
-  // lane (g, i) supplies keys {4g + i/4} x dims {16 dt + 4 (i%4) .. +3}; receives dim
-  // 16 dt + i of keys 4g .. 4g+3 (lo) and 16 + 4g .. 16 + 4g + 3 (hi).
-  const _Float16* vbase = ks_tile + (4 * g16 + (c16 >> 2)) * kKS + 256 * DH + 4 * (c16 & 3);
+// O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.  V^T fragments
+// come straight from the e4m3 rows through ds_read_b64_tr_b8: in lane group g, lane pair
+// (2e, 2e+1) addresses row kp(g, e) = 16 (e >> 2) + 4 g + (e & 3) (bytes 8 (lane & 1) of the
+// fragment's 16 dims), and lane (g, i) receives dim i of rows kp(g, 0..7) -- the key order of
+// the P^T operand taken from the S^T accumulators in place.
+template <int ROPE, int DH>
+__device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&pv)[2][2][4],
+                                        f32x4 (&o_acc)[2][16], bool& sc_bad, int g16,
+                                        int c16) {
+  constexpr int RS = MlaGeom<ROPE>::RS;
+  const int e2 = c16 >> 1;
+  const int kp = 16 * (e2 >> 2) + 4 * g16 + (e2 & 3);
+  const unsigned char* vbase = raw + kp * RS + 256 * DH + 8 * (c16 & 1);
 #pragma unroll
   for (int b2 = 0; b2 < 2; ++b2) {
     const int blk = 2 * DH + b2;
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc_tile + blk * kTK + 4 * g16);
-    const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc_tile + blk * kTK + 16 + 4 * g16);
+    float vsc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vsc[e] = *reinterpret_cast<const float*>(
+          raw + (16 * (e >> 2) + 4 * g16 + (e & 3)) * RS + kScaleOff + 4 * blk);
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    auto read_v = [&](int dd) {
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(const_cast<unsigned char*>(
+              vbase + 16 * (b2 * 8 + dd))));
+    };
+    v2i vw[8];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) vw[dd] = read_v(dd);
     f16x8 pb[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc_bad |= !(fabsf(vsc[e]) <= kMaxVScale);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pb[ht][j] = (_Float16)(pv[ht][0][j] * v0[j]);
-        pb[ht][4 + j] = (_Float16)(pv[ht][1][j] * v1[j]);
-      }
+      for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       __builtin_amdgcn_sched_barrier(0);
-      const _Float16* src0 = vbase + 16 * (b2 * 8 + dd);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0)));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(lds_short*)(const_cast<_Float16*>(src0 + 16 * kKS)));
-      const s16x8 w8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const f16x8 va = __builtin_bit_cast(f16x8, w8);
+      if (dd + 4 < 8) vw[dd + 4] = read_v(dd + 4);
+      const v2i w = vw[dd];
+      const f16x4 lo = e4m3x4_to_f16((uint32_t)w[0]), hi = e4m3x4_to_f16((uint32_t)w[1]);
+      const f16x8 va{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o_acc[0][b2 * 8 + dd] = mfma_f16(va, pb[0], o_acc[0][b2 * 8 + dd]);
       o_acc[1][b2 * 8 + dd] = mfma_f16(va, pb[1], o_acc[1][b2 * 8 + dd]);
     }
@@ -194,11 +236,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   using G = MlaGeom<ROPE>;
   constexpr int NT = kMlaThreads;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* ks_tile = reinterpret_cast<_Float16*>(smem + G::OFF_KS);
-  float* sc_tile = reinterpret_cast<float*>(smem + G::OFF_SC);
-  float* mask_tile = reinterpret_cast<float*>(smem + G::OFF_MASK);
   f32x4* xs = reinterpret_cast<f32x4*>(smem + G::OFF_XS);
-  _Float16* qr_sh = reinterpret_cast<_Float16*>(smem + G::OFF_QR);
+  __bf16* qr_sh = reinterpret_cast<__bf16*>(smem + G::OFF_QR);
   int* slot_sh = reinterpret_cast<int*>(smem + G::OFF_SLOT);
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
@@ -250,27 +289,16 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     }
     slot_sh[i] = slot;
   }
-  // RoPE query of the group's heads, as fp16, into LDS.
+  // RoPE query of the group's heads (bf16, as given) into LDS.
   if (ROPE) {
-    bool ok = true;
     for (int i = tid; i < kHeadsPerWg * 8; i += NT) {
       const int hh = i >> 3, q8 = i & 7;
-      f16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
-      if (hbase + hh < H) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (hbase + hh < H)
+        v = *reinterpret_cast<const u32x4*>(
             static_cast<const __bf16*>(a.q) + ((size_t)r * H + hbase + hh) * 576 + 512 + 8 * q8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = (float)x[e];
-          ok &= fabsf(f) <= kF16Max;
-          v[e] = (_Float16)f;
-        }
-      }
-      *reinterpret_cast<f16x8*>(qr_sh + hh * kQRS + 8 * q8) = v;
+      *reinterpret_cast<u32x4*>(qr_sh + hh * kQRS + 8 * q8) = v;
     }
-    if (!ok) raise_fault(a.fault, kFaultRange);
   }
   __syncthreads();
 
@@ -279,19 +307,24 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   // on a masked key read zeros instead.  Every wave issues exactly PER_WAVE transfers per
   // tile, which the vmcnt waits below rely on.
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
+  const uint8_t* zero_row = g_zero_row;
+  asm volatile("" : "+s"(zero_row));   // loaded once, not re-fetched from the GOT per tile
   auto issue = [&](int tile, int lane) {
     const uint32_t stage = lds0 + (uint32_t)((tile % kNStage) * G::STAGE);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int slot[G::PER_WAVE], off[G::PER_WAVE];
+#pragma unroll
+    for (int u = 0; u < G::PER_WAVE; ++u) {
+      const int f = (wv + u * kMlaWaves) * kWave + lane;
+      const int kk = min(f / G::NCH, kTK - 1);
+      off[u] = 16 * (f - (f / G::NCH) * G::NCH);
+      slot[u] = slot_sh[tile * kTK + kk];
+      if (f >= G::RAW) slot[u] = -1;
+    }
 #pragma unroll
     for (int u = 0; u < G::PER_WAVE; ++u) {
       const int m = wv + u * kMlaWaves;
-      const int f = m * kWave + lane;
-      const uint8_t* src = g_zero_row;
-      if (f < G::RAW) {
-        const int kk = f / G::NCH, j = f - (f / G::NCH) * G::NCH;
-        const int slot = slot_sh[tile * kTK + kk];
-        if (slot >= 0) src = pool + (int64_t)slot * kLatRow + 16 * j;
-      }
+      const uint8_t* src = slot[u] >= 0 ? pool + (int64_t)slot[u] * kLatRow + off[u] : zero_row;
       const uint32_t dst = m < G::NBLK ? stage + (uint32_t)(m * 1024) : lds0 + G::OFF_JUNK;
       dma16(src, dst);
     }
@@ -329,90 +362,36 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     for (int i = 0; i < 16; ++i) o_acc[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
   float l_part[2] = {0.f, 0.f};
+  bool sc_bad = false;   // a latent scale that could push P * scale out of fp16
 
-  if (ntiles > 0) issue(0, lane0);
-  if (ntiles > 1) issue(1, lane0);
+#pragma unroll
+  for (int t = 0; t < kNStage - 1; ++t)
+    if (t < ntiles) issue(t, lane0);
   for (int tile = 0; tile < ntiles; ++tile) {
     // Lane-derived addresses are recomputed every tile (a few VALU instructions) rather than
     // hoisted out of the loop: the query and the accumulator leave no registers to keep them.
     int lane = lane0;
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, c16 = lane & 15;
-    const _Float16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
-    if (tile + 2 < ntiles) issue(tile + 2, lane);
-    const int ahead = min(2, ntiles - 1 - tile);
-    if (ahead == 2) wait_vmcnt<2 * G::PER_WAVE>();
+    const unsigned char* raw = smem + (tile % kNStage) * G::STAGE;
+    // This tile's transfers are the oldest outstanding ones: later tiles may stay in flight.
+    const int ahead = min(kNStage - 2, ntiles - 1 - tile);
+    if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
     else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
     else wait_vmcnt<0>();
-    __syncthreads();   // every wave's transfers of this tile landed; last tile's math done
-
-    // ---- staging: raw e4m3 rows -> exact fp16 tile, per-128 scales, key masks.  Masked
-    //      keys were gathered from a zero row, so no per-chunk check is needed.  Each thread
-    //      converts two 16-byte latent chunks and at most one scale / RoPE chunk; all LDS
-    //      reads are issued before the conversions.
-    {
-      constexpr int NX = G::NCH - 32;                // scale + RoPE chunks per key
-      const unsigned char* src = smem + (tile % kNStage) * G::STAGE;
-      int tid = tid0;
-      asm volatile("" : "+v"(tid));                  // recomputed per tile, not hoisted
-      u32x4 v[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = tid + u * NT;                  // latent chunk i: key i >> 5, chunk i & 31
-        v[u] = *reinterpret_cast<const u32x4*>(src + 16 * ((i >> 5) * G::NCH + (i & 31)));
-      }
-      const bool has_x = tid < kTK * NX;
-      const int xk = tid / NX, xj = tid - (tid / NX) * NX;
-      u32x4 w = u32x4{0, 0, 0, 0};
-      if (has_x) w = *reinterpret_cast<const u32x4*>(src + 16 * (xk * G::NCH + 32 + xj));
-      int slot = 0;
-      if (tid < kTK) slot = slot_sh[tile * kTK + tid];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = tid + u * NT;
-        _Float16* kd = ks_tile + (i >> 5) * kKS + 16 * (i & 31);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f16x4 f0 = e4m3x4_to_f16(v[u][2 * h]), f1 = e4m3x4_to_f16(v[u][2 * h + 1]);
-          *reinterpret_cast<f16x8*>(kd + 8 * h) =
-              f16x8{f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-        }
-      }
-      if (has_x) {
-        bool in_range = true;
-        if (xj == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sc = __uint_as_float(w[e]);
-            in_range &= fabsf(sc) <= kMaxVScale;
-            sc_tile[e * kTK + xk] = sc;
-          }
-        } else {
-          const bf16x8 rb = __builtin_bit_cast(bf16x8, w);
-          f16x8 rh;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f2 = (float)rb[e];
-            in_range &= fabsf(f2) <= kF16Max;
-            rh[e] = (_Float16)f2;
-          }
-          *reinterpret_cast<f16x8*>(ks_tile + xk * kKS + 512 + 8 * (xj - 1)) = rh;
-        }
-        if (!in_range) raise_fault(a.fault, kFaultRange);
-      }
-      if (tid < kTK) mask_tile[tid] = slot >= 0 ? 0.f : -__builtin_inff();
-    }
-    __syncthreads();
+    __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
+    if (tile + kNStage - 1 < ntiles) issue(tile + kNStage - 1, lane);
 
     // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
     //      partner waves then add half 0 + half 1 in the same order
     {
+      const __bf16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
       f32x4* mine = xs + wave * 4 * kWave;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 sk[2];
-        if (dh == 0) qk_part<ROPE, 0>(ks_tile, sc_tile, qr_lane, qb, kt, sk, g16, c16);
-        else qk_part<ROPE, 1>(ks_tile, sc_tile, qr_lane, qb, kt, sk, g16, c16);
+        if (dh == 0) qk_part<ROPE, 0>(raw, qr_lane, qb, kt, sk, g16, c16);
+        else qk_part<ROPE, 1>(raw, qr_lane, qb, kt, sk, g16, c16);
         mine[(2 * kt) * kWave + lane] = sk[0];
         mine[(2 * kt + 1) * kWave + lane] = sk[1];
       }
@@ -422,8 +401,10 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     {
       const f32x4* p0 = xs + hg * 4 * kWave;
       const f32x4* p1 = xs + (hg | 4) * 4 * kWave;
-      const f32x4 mk0 = *reinterpret_cast<const f32x4*>(mask_tile + 4 * g16);
-      const f32x4 mk1 = *reinterpret_cast<const f32x4*>(mask_tile + 16 + 4 * g16);
+      const int* sl = slot_sh + tile * kTK + 4 * g16;
+      const int4 s0 = *reinterpret_cast<const int4*>(sl);
+      const int4 s1 = *reinterpret_cast<const int4*>(sl + 16);
+      const int sv[2][4] = {{s0.x, s0.y, s0.z, s0.w}, {s1.x, s1.y, s1.z, s1.w}};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -431,7 +412,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
           const f32x4 sum = p0[(2 * kt + ht) * kWave + lane] + p1[(2 * kt + ht) * kWave + lane];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            pv[ht][kt][j] = fmaf(sum[j], qk_scale, kt ? mk1[j] : mk0[j]);
+            pv[ht][kt][j] = sv[kt][j] >= 0 ? sum[j] * qk_scale : -__builtin_inff();
         }
     }
 
@@ -443,8 +424,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mt = fmaxf(mt, pv[ht][kt][j]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_over_lane_groups(mt);
       const bool need = mt > m_run[ht] + kRescaleSlack || (m_run[ht] == -__builtin_inff() && mt > m_run[ht]);
       if (__any(need)) {
         const float m_new = need ? fmaxf(m_run[ht], mt) : m_run[ht];
@@ -468,22 +448,23 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T over this wave's dim half
-    if (dh == 0) pv_part<0>(ks_tile, sc_tile, pv, o_acc, g16, c16);
-    else pv_part<1>(ks_tile, sc_tile, pv, o_acc, g16, c16);
+    if (dh == 0) pv_part<ROPE, 0>(raw, pv, o_acc, sc_bad, g16, c16);
+    else pv_part<ROPE, 1>(raw, pv, o_acc, sc_bad, g16, c16);
   }
+
+  if (__any(sc_bad) && lane0 == 0) raise_fault(a.fault, kFaultRange);
 
   // ---- epilogue: lane (g, i) holds O[head h0 + 16 ht + i][dims 256 dh + 16 t + 4 g + j]
   if (!active) return;
+  const int g16e = lane0 >> 4, c16e = lane0 & 15;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     if (!ht_live[ht]) continue;
-    float l = l_part[ht];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int h = h0 + 16 * ht + c16;
+    const float l = sum_over_lane_groups(l_part[ht]);
+    const int h = h0 + 16 * ht + c16e;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse2 = l > 0.f ? m_run[ht] + log2f(l) : -__builtin_inff();
-    const int d0 = 256 * dh + 4 * g16;
+    const int d0 = 256 * dh + 4 * g16e;
     if (nsplit == 1) {
       __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)r * H + h) * 512 + d0;
 #pragma unroll
@@ -492,7 +473,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         *reinterpret_cast<bf16x4*>(out + 16 * i) =
             bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
-      if (a.lse && g16 == 0 && dh == 0) a.lse[(size_t)r * H + h] = lse2 * kLn2;
+      if (a.lse && g16e == 0 && dh == 0) a.lse[(size_t)r * H + h] = lse2 * kLn2;
     } else {
       float* po = part + (((size_t)r * H + h) * nsplit + split) * 513;
 #pragma unroll
@@ -500,9 +481,12 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         const f32x4 v = o_acc[ht][i] * inv;
         *reinterpret_cast<f32x4*>(po + d0 + 16 * i) = v;
       }
-      if (g16 == 0 && dh == 0) po[512] = lse2;
+      if (g16e == 0 && dh == 0) po[512] = lse2;
     }
   }
+  (void)tid0;
+  (void)g16;
+  (void)c16;
 }
 
 template <int ROPE>
