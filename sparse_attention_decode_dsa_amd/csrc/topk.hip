@@ -13,9 +13,11 @@
 //      known (or its bucket is taken whole).
 //   3. Ordered compaction in ascending t: keys above the threshold are kept; keys equal to it
 //      are kept lowest-t first until k are chosen (wave ballots + block prefix sums).
-// Rows up to 32,768 keys cache their keys in LDS after the first read; longer rows stream
-// from L2.  Rows longer than 131,072 keys use a multi-work-group version with the same
-// steps, one launch per step, its histograms merged with integer atomics.
+// Rows up to 131,072 positions first narrow the row to an LDS candidate list with a
+// threshold taken from a sample (one read of the row), and run steps 2-3 on that list; the
+// streaming form above is their fallback when the list misses.  Longer rows use a
+// multi-work-group version with the same steps, one launch per step, its histograms merged
+// with integer atomics.
 #include "ml4_device.h"
 
 namespace ml4 {
@@ -168,9 +170,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Exact selection for row r with n > K candidates, streaming the row (CACHE: keys kept in
+// kcache after the first read).  Called by every thread of a kRowThreads work-group.
 template <bool CACHE>
-__global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
-  extern __shared__ uint32_t kcache[];
+__device__ void row_select_exact(const TopkLaunch& a, int r, int n, uint32_t* kcache) {
   constexpr int NW = kRowThreads / kWave;
   __shared__ uint32_t hist[1 << kMaxDigitBits];
   __shared__ int sh_scan[NW];
@@ -179,9 +182,6 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   __shared__ int sh_nan;
   __shared__ int sh_gt[NW], sh_eq[NW];
 
-  const int r = blockIdx.x;
-  int n = 0;
-  if (!row_prologue(a, r, &n)) return;
   const int K = a.top_k;
   const float* row = a.scores + (size_t)r * a.ld;
   const int tid = threadIdx.x;
@@ -323,6 +323,193 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
       }
     carry_eq += __shfl(eq_incl, kWave - 1);
     carry_out += __shfl(s_incl, kWave - 1);
+  }
+  if (tid == 0) a.len[r] = K;
+}
+
+// ------------------------------------------------------------ candidate filter, one row per WG
+// 1. Threshold from a sample: every (n4 / 1024)-th float4 of the row (4,096 keys); T = the
+//    key of rank ~1.5 K n_s / n among them, so that about 1.5 K keys of the row are >= T.
+// 2. One pass over the row appends every key >= T, with its position, to an LDS list
+//    (wave-aggregated slots).  If the list holds fewer than K or more than kCand keys the
+//    row falls back to the streaming exact selection; otherwise the top K of the row are
+//    exactly the top K of the list (every key outside the list is below T).
+// 3. Radix select on the list gives the K-th key and how many keys equal to it to keep; a
+//    bitmap over positions then yields the kept positions in ascending order, keys equal
+//    to the K-th taken lowest position first.
+constexpr int kCand = 8192;
+constexpr int kMaxCandRow = 4 * kCacheKeys;     // 131,072 positions: 4,096 bitmap words
+constexpr int kSampleVec = 1024;
+
+// rank-th largest (1-based) of keys[0 .. m) in LDS: returns that key and writes into *above
+// the number of keys strictly greater.  Every thread of the work-group must call it.
+__device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above_out,
+                               uint32_t* hist, int* sh_scan, int* sh_sel) {
+  uint32_t P = 0;        // bits of the answer above `shift`
+  int shift = 32, need = rank, above_total = 0;
+  while (shift > 0) {
+    const int w = min(kMaxDigitBits, shift);
+    const int nsh = shift - w;
+    const int nb = 1 << w;
+    for (int i = threadIdx.x; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < m; i += kRowThreads) {
+      const uint32_t k = keys[i];
+      if (digit_prefix(k, shift) == P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    const int d = sh_sel[0], above = sh_sel[1];
+    __syncthreads();
+    P = (uint32_t)((P << w) | (uint32_t)d);
+    need -= above;
+    above_total += above;
+    shift = nsh;
+  }
+  *above_out = above_total;
+  return P;
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
+  constexpr int NW = kRowThreads / kWave;
+  __shared__ uint32_t cand_key[kCand];
+  __shared__ int cand_t[kCand];
+  __shared__ uint32_t sel_bits[kMaxCandRow / 32], tie_bits[kMaxCandRow / 32];
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ int sh_scan[NW];
+  __shared__ int sh_sel[4];
+  __shared__ int sh_count, sh_nan;
+
+  const int r = blockIdx.x;
+  int n = 0;
+  if (!row_prologue(a, r, &n)) return;
+  const int K = a.top_k;
+  const float* row = a.scores + (size_t)r * a.ld;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int n4 = (n + 3) >> 2;
+
+  // 1. threshold
+  uint32_t T = 0u;
+  if (n > kCand) {
+    const int j = tid;   // one float4 per thread
+    const int i4 = (int)(((long long)j * n4) / kSampleVec);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool nn = false;
+      const uint32_t k = order_key(v[e], nn);
+      cand_key[4 * j + e] = (4 * i4 + e < n) ? k : 0u;
+    }
+    __syncthreads();
+    const int ns = 4 * kSampleVec;
+    const int rank = min(ns, (int)(1.5f * (float)K * (float)ns / (float)n) + 8);
+    int above;
+    T = lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel);
+  }
+
+  // 2. candidate list
+  if (tid == 0) { sh_count = 0; sh_nan = 0; }
+  __syncthreads();
+  bool any_nan = false;
+  for (int base = tid; base - tid < n4; base += kRowThreads * kU) {
+    uint32_t kv[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+      if (i4 < n4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bool nn = false;
+          kv[u][e] = order_key(v[e], nn);
+          any_nan |= nn && 4 * i4 + e < n;
+        }
+      }
+    }
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += (i4 < n4 && 4 * i4 + e < n && kv[u][e] >= T) ? 1 : 0;
+    }
+    const int incl = wave_incl_scan(c);
+    int slot = 0;
+    if (lane == kWave - 1) slot = atomicAdd(&sh_count, incl);
+    slot = __shfl(slot, kWave - 1) + incl - c;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = base + u * kRowThreads;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i4 < n4 && 4 * i4 + e < n && kv[u][e] >= T) {
+          if (slot < kCand) {
+            cand_key[slot] = kv[u][e];
+            cand_t[slot] = 4 * i4 + e;
+          }
+          ++slot;
+        }
+    }
+  }
+  if (any_nan) sh_nan = 1;
+  __syncthreads();
+  const int m = sh_count;
+  if (tid == 0 && sh_nan) raise_fault(a.fault, kFaultNan);
+  if (m < K || m > kCand) {    // threshold missed: exact selection over the whole row
+    __syncthreads();
+    row_select_exact<false>(a, r, n, nullptr);
+    return;
+  }
+
+  // 3. K-th key of the list, then the kept positions in ascending order
+  int above;
+  const uint32_t kth = lds_select(cand_key, m, K, &above, hist, sh_scan, sh_sel);
+  const int need_eq = K - above;          // keys equal to kth to keep, lowest position first
+  const int nw = (n + 31) >> 5;
+  for (int i = tid; i < nw; i += kRowThreads) { sel_bits[i] = 0u; tie_bits[i] = 0u; }
+  __syncthreads();
+  for (int i = tid; i < m; i += kRowThreads) {
+    const uint32_t k = cand_key[i];
+    const int t = cand_t[i];
+    if (k > kth) atomicOr(&sel_bits[t >> 5], 1u << (t & 31));
+    else if (k == kth) atomicOr(&tie_bits[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  // thread tid owns words [wpt * tid, wpt * tid + wpt)
+  constexpr int kWpt = kMaxCandRow / 32 / kRowThreads;   // 4
+  const int w0 = kWpt * tid;
+  int my_ties = 0;
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) my_ties += (w0 + q < nw) ? __builtin_popcount(tie_bits[w0 + q]) : 0;
+  int tot;
+  int tie_rank = block_exclusive_scan<kRowThreads>(my_ties, &tot, sh_scan);
+  uint32_t keep[kWpt];
+  int my_sel = 0;
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) {
+    uint32_t sb = (w0 + q < nw) ? sel_bits[w0 + q] : 0u;
+    uint32_t tb = (w0 + q < nw) ? tie_bits[w0 + q] : 0u;
+    while (tb) {                                 // ties in ascending position
+      const uint32_t low = tb & (0u - tb);
+      if (tie_rank < need_eq) sb |= low;
+      ++tie_rank;
+      tb ^= low;
+    }
+    keep[q] = sb;
+    my_sel += __builtin_popcount(sb);
+  }
+  int at = block_exclusive_scan<kRowThreads>(my_sel, &tot, sh_scan);
+  int32_t* out = a.idx + (size_t)r * K;
+#pragma unroll
+  for (int q = 0; q < kWpt; ++q) {
+    uint32_t sb = keep[q];
+    while (sb) {
+      const int bit = __builtin_ctz(sb);
+      if (at < K) out[at] = 32 * (w0 + q) + bit;
+      ++at;
+      sb &= sb - 1;
+    }
   }
   if (tid == 0) a.len[r] = K;
 }
@@ -549,7 +736,6 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chu
   }
 }
 
-bool lds_attr_set = false;
 
 }  // namespace
 
@@ -565,19 +751,8 @@ size_t topk_ws_bytes(const SeqView& s, int top_k) {
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   const SeqView& s = a.s;
-  if (s.max_seq_len <= kCacheKeys) {
-    const size_t lds = (size_t)kCacheKeys * 4;
-    if (!lds_attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_row<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      lds_attr_set = true;
-    }
-    k_topk_row<true><<<s.total_q, kRowThreads, lds, st>>>(a);
-    return hipGetLastError();
-  }
-  if (s.max_seq_len <= 4 * kCacheKeys) {
-    k_topk_row<false><<<s.total_q, kRowThreads, 0, st>>>(a);
+  if (s.max_seq_len <= kMaxCandRow) {
+    k_topk_cand<<<s.total_q, kRowThreads, 0, st>>>(a);
     return hipGetLastError();
   }
   const int chunks = big_chunks(s);

@@ -185,6 +185,36 @@ def test_topk_exact_on_given_scores(n, top_k, seed):
         assert np.array_equal(gi[r], oi), f"row {r}: first diff at {np.argmax(gi[r] != oi)}"
 
 
+@pytest.mark.parametrize("n,top_k,kind", [(20000, 2048, "const"), (50000, 2048, "tie_block"),
+                                          (9000, 2048, "const")])
+def test_topk_when_the_candidate_list_overflows(n, top_k, kind):
+    """Rows whose keys above the sampled threshold do not fit the candidate list (massive
+    ties at the threshold) take the streaming selection; the result is still the oracle's."""
+    _say(f"[gpu] topk overflow n={n} k={top_k} {kind}")
+    g = torch.Generator().manual_seed(n)
+    if kind == "const":
+        x = torch.full((n,), 0.25)
+    else:
+        x = torch.clamp(torch.randn(n, generator=g), max=2.9)
+        x[torch.randperm(n, generator=g)[:9000]] = 3.0
+    ld = (n + 3) // 4 * 4
+    scores = torch.full((1, ld), -5.0)
+    scores[0, :n] = x
+    batch = synth.make_batch(1, [n], [1], 64, device=DEV)
+    seqs = M.make_seqs(batch)
+    idx = torch.full((1, top_k), -9, dtype=torch.int32, device=DEV)
+    ln = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_TOPK, seqs, 0, top_k)
+    ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=DEV)
+    fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+    M.ml4_topk_select(seqs, scores.to(DEV), ld, top_k, idx, ln, ws, wsn, fault)
+    torch.cuda.synchronize()
+    assert M.ml4_fault_query(fault) == 0
+    oi, on = O.topk_row(scores.numpy()[0].astype(np.float64), n - 1, top_k)
+    assert t_np(ln)[0] == on
+    assert np.array_equal(t_np(idx)[0], oi)
+
+
 def _topk_lists(case, seed, top_k):
     """Seeded selections: distinct ascending positions in [0, p] per row, ragged lengths."""
     g = np.random.default_rng(seed)
