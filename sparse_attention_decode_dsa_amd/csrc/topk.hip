@@ -329,7 +329,8 @@ __device__ void row_select_exact(const TopkLaunch& a, int r, int n, uint32_t* kc
 
 // ------------------------------------------------------------ candidate filter, one row per WG
 // 1. Threshold from a sample: every (n4 / 1024)-th float4 of the row (4,096 keys); T = the
-//    key of rank ~1.5 K n_s / n among them, so that about 1.5 K keys of the row are >= T.
+//    key of rank ~1.5 K n_s / n among them to 22 leading bits, so that about 1.5 K keys of
+//    the row are >= T.
 // 2. One pass over the row appends every key >= T, with its position, to an LDS list
 //    (wave-aggregated slots).  If the list holds fewer than K or more than kCand keys the
 //    row falls back to the streaming exact selection; otherwise the top K of the row are
@@ -343,11 +344,14 @@ constexpr int kSampleVec = 1024;
 
 // rank-th largest (1-based) of keys[0 .. m) in LDS: returns that key and writes into *above
 // the number of keys strictly greater.  Every thread of the work-group must call it.
+// With stop_shift > 0 the search ends once the bits above stop_shift are known and the
+// result has its low stop_shift bits cleared (a lower bound of that key; *above is then
+// not meaningful).
 __device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above_out,
-                               uint32_t* hist, int* sh_scan, int* sh_sel) {
+                               uint32_t* hist, int* sh_scan, int* sh_sel, int stop_shift = 0) {
   uint32_t P = 0;        // bits of the answer above `shift`
   int shift = 32, need = rank, above_total = 0;
-  while (shift > 0) {
+  while (shift > stop_shift) {
     const int w = min(kMaxDigitBits, shift);
     const int nsh = shift - w;
     const int nb = 1 << w;
@@ -367,7 +371,7 @@ __device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above
     shift = nsh;
   }
   *above_out = above_total;
-  return P;
+  return shift > 0 ? P << shift : P;
 }
 
 __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
@@ -389,7 +393,16 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
   const int lane = tid & (kWave - 1);
   const int n4 = (n + 3) >> 2;
 
-  // 1. threshold
+  // The first batch of the candidate pass is loaded before the threshold is known, so its
+  // latency overlaps the sample selection.
+  f32x4 first[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int i4 = tid + u * kRowThreads;
+    first[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(row + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // 1. threshold (22 leading bits are enough; the low 10 are left clear)
   uint32_t T = 0u;
   if (n > kCand) {
     const int j = tid;   // one float4 per thread
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
     const int ns = 4 * kSampleVec;
     const int rank = min(ns, (int)(1.5f * (float)K * (float)ns / (float)n) + 8);
     int above;
-    T = lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel);
+    T = lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel, 10);
   }
 
   // 2. candidate list
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
     for (int u = 0; u < kU; ++u) {
       const int i4 = base + u * kRowThreads;
       if (i4 < n4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+        const f32x4 v = base == tid ? first[u] : *reinterpret_cast<const f32x4*>(row + 4 * i4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bool nn = false;
