@@ -39,6 +39,16 @@ Page titles used below:
    [blog, ROCm implementation details › "AITER 上的稀疏 MLA" (top-2048 positions become
    global cache slots, one entry per query token)].
 
+6. KV-cache writes (the step before the path)  [blog, ROCm implementation details ›
+   "AITER 上的 DSA 索引器" (FP8 indexer key with one scale per key, 132 B); "FP8 潜在缓存"
+   (fp8_ds_mla: 512 FP8 values with four scales, one per 128, and 64 bf16 RoPE values,
+   656 B)].  The pages fix the byte layout but not the quantiser; the reading taken is the
+   plain symmetric one: per scale group, scale = amax / 448 (448 = largest E4M3 value) and
+   code = E4M3(x / scale) rounded to nearest, ties to even, clamped to +-448; an all-zero
+   group gets scale 0 and zero codes.  The code is an integer decided by floating point,
+   so it is decided in the kernel's precision: amax, the scale and x / scale are binary32
+   operations (each correctly rounded), only the final E4M3 rounding is done here.
+
 Every step is the plain definition, in fp64, in the pages' order; numpy matrix products
 serve as the only library primitive.
 """
@@ -368,3 +378,74 @@ def kv_bytes_per_token(latent_row: int, index_row: int = IDX_ROW_FP8) -> int:
     owners = N_LAYERS - len(KV_CONSUMERS)
     indexers = N_LAYERS - N_INDEX_SHARERS
     return owners * latent_row + indexers * index_row
+
+
+# --------------------------------------------------------------------------------------
+# 6. KV-cache writes: quantise and pack rows  [blog, "AITER 上的 DSA 索引器"; "FP8 潜在缓存"]
+# --------------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """binary32 values already inside [-448, 448] -> OCP E4M3 codes, round to nearest with
+    ties to even.  The grid is 2^-9 steps below 2^-6 (subnormals) and 8 steps per binade
+    above; the sign of zero is kept."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    assert np.all(np.isfinite(v)) and np.all(np.abs(v) <= E4M3_MAX)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    a = np.abs(v)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal binade: value = m * 2^-9, m in 0..8 (m = 8 is the smallest normal, code 8)
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub
+    if np.any(nrm):
+        m, e = np.frexp(a[nrm])                  # a = m * 2^e, m in [0.5, 1)
+        e = e - 1                                # a = (2m) * 2^e, 2m in [1, 2)
+        q = np.rint(2.0 * m * 8.0).astype(np.int64)   # 8 .. 16 (ties to even)
+        up = q == 16
+        e = np.where(up, e + 1, e)
+        q = np.where(up, 8, q)
+        code[nrm] = ((e + 7) << 3) | (q - 8)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def _quantise_group(x32: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """One scale group (binary32 values) -> (codes, scale)."""
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    scale = np.float32(amax / np.float32(E4M3_MAX))
+    if scale == 0:
+        return np.zeros(x32.shape, dtype=np.uint8), np.float32(0.0)
+    v = (x32 / scale).astype(np.float32)                 # binary32 division
+    v = np.clip(v, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return encode_e4m3(v), scale
+
+
+def quantise_index_rows(k32: np.ndarray) -> np.ndarray:
+    """[n][128] binary32 keys -> [n][132] rows: 128 E4M3 codes then the fp32 key scale."""
+    k32 = np.asarray(k32, dtype=np.float32)
+    out = np.zeros((k32.shape[0], IDX_ROW_FP8), dtype=np.uint8)
+    for i in range(k32.shape[0]):
+        codes, sc = _quantise_group(k32[i])
+        out[i, :IDX_DIM] = codes
+        out[i, IDX_DIM:] = np.frombuffer(np.float32(sc).tobytes(), dtype=np.uint8)
+    return out
+
+
+def quantise_latent_rows(c32: np.ndarray, rope_bf16_bits: Optional[np.ndarray]) -> np.ndarray:
+    """[n][512] binary32 latents (+ [n][64] bf16 RoPE bits, or None) -> [n][656] rows:
+    512 E4M3 codes, four fp32 scales (one per 128 codes), 64 bf16 RoPE values (left zero
+    here when None: a NoPE write does not touch those bytes)."""
+    c32 = np.asarray(c32, dtype=np.float32)
+    out = np.zeros((c32.shape[0], LAT_ROW_FP8), dtype=np.uint8)
+    ng = KV_LORA // LAT_SCALE_GROUP
+    for i in range(c32.shape[0]):
+        for g in range(ng):
+            codes, sc = _quantise_group(c32[i, g * LAT_SCALE_GROUP:(g + 1) * LAT_SCALE_GROUP])
+            out[i, g * LAT_SCALE_GROUP:(g + 1) * LAT_SCALE_GROUP] = codes
+            out[i, KV_LORA + 4 * g:KV_LORA + 4 * g + 4] = np.frombuffer(
+                np.float32(sc).tobytes(), dtype=np.uint8)
+        if rope_bf16_bits is not None:
+            out[i, KV_LORA + 4 * ng:] = np.frombuffer(
+                np.asarray(rope_bf16_bits[i], dtype="<u2").tobytes(), dtype=np.uint8)
+    return out

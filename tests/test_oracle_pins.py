@@ -382,3 +382,80 @@ def test_layer_modes_consumer_and_shared_indexer():
     o2, l2, i2, _ = O.layer_step(L2, s, "fp8", {0: pool0, 1: pool1}, {2: ipool}, qi, None, w,
                                  q, store, ld=64)
     assert np.array_equal(o2, o0) and np.array_equal(i2, i0)   # same indexer inputs here
+
+
+# ---------------------------------------------------------------- KV-cache writes (quantiser)
+def _e4m3_grid():
+    vals = np.array(sorted({float(v) for v in O.E4M3_TABLE if np.isfinite(v) and v >= 0}))
+    return vals
+
+
+def test_e4m3_encoder_matches_torch_round_to_nearest_even():
+    """Every finite E4M3 value, every midpoint between neighbours (ties), a quarter either
+    side of each midpoint, and random binary32 values in range: the encoder's codes equal
+    torch's float8_e4m3fn cast (round to nearest, ties to even) bit for bit."""
+    pos = _e4m3_grid()
+    mids = (pos[:-1] + pos[1:]) / 2
+    quarter = (pos[1:] - pos[:-1]) / 4
+    g = np.random.default_rng(3)
+    rnd = g.uniform(-448, 448, 20000)
+    small = g.uniform(-2.0 ** -5, 2.0 ** -5, 5000)
+    x = np.concatenate([pos, -pos, mids, -mids, mids - quarter, mids + quarter,
+                        -(mids + quarter), rnd, small]).astype(np.float32)
+    got = O.encode_e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    # decoding the code returns an exactly representable value unchanged
+    assert np.array_equal(O.decode_e4m3(O.encode_e4m3(pos.astype(np.float32))), pos)
+
+
+def test_e4m3_encoder_ties_go_to_even_codes():
+    assert list(O.encode_e4m3(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 272.0],
+                                       dtype=np.float32))) == [0x38, 0x3A, 0x00, 0x02, 0x78]
+    assert O.encode_e4m3(np.array([-0.0], dtype=np.float32))[0] == 0x80
+
+
+def test_index_row_quantiser_layout_scale_and_error_bound():
+    g = np.random.default_rng(5)
+    k = (g.standard_normal((64, 128)) * np.exp(g.uniform(-6, 6, (64, 1)))).astype(np.float32)
+    k[3] = 0.0                                            # all-zero key
+    rows = O.quantise_index_rows(k)
+    assert rows.shape == (64, 132)
+    codes, scale = rows[:, :128], rows[:, 128:].copy().view("<f4")[:, 0]
+    amax = np.abs(k).max(axis=1).astype(np.float32)
+    assert np.array_equal(scale, (amax / np.float32(448.0)).astype(np.float32))
+    assert np.all(codes[3] == 0) and scale[3] == 0
+    # the largest element of every non-zero key lands on +-448
+    live = amax > 0
+    top = np.abs(k).argmax(axis=1)
+    assert np.all(np.isin(codes[live, top[live]], [0x7E, 0xFE]))
+    # dequantised error: half an E4M3 step (2^-4 relative, 2^-10 absolute below 2^-6)
+    deq = O.decode_e4m3(codes) * scale[:, None]
+    bound = np.maximum(np.abs(k) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
+    assert np.all(np.abs(deq - k) <= bound)
+    # the indexer reader decodes what the writer packed
+    pool = rows.reshape(1, 64, 132)
+    kk, ks = O.index_rows_fp8(pool, np.arange(64))
+    assert np.allclose(kk * ks[:, None], deq, rtol=0, atol=0)
+
+
+def test_latent_row_quantiser_groups_rope_and_reader_round_trip():
+    g = np.random.default_rng(6)
+    c = (g.standard_normal((16, 512)) * np.repeat(np.exp(g.uniform(-4, 4, (16, 4))), 128, axis=1)
+         ).astype(np.float32)
+    c[5, 128:256] = 0.0                                   # one all-zero scale group
+    rope = P.bf16_bits(torch.randn(16, 64, generator=torch.Generator().manual_seed(2)))
+    rows = O.quantise_latent_rows(c, rope)
+    assert rows.shape == (16, 656)
+    scales = rows[:, 512:528].copy().view("<f4")
+    for gi in range(4):
+        amax = np.abs(c[:, 128 * gi:128 * (gi + 1)]).max(axis=1).astype(np.float32)
+        assert np.array_equal(scales[:, gi], (amax / np.float32(448.0)).astype(np.float32))
+    assert scales[5, 1] == 0 and np.all(rows[5, 128:256] == 0)
+    assert np.array_equal(rows[:, 528:].copy().view("<u2"), rope.astype(np.uint16))
+    cc, kr = O.latent_rows_fp8(rows.reshape(1, 16, 656), np.arange(16), 64)
+    bound = np.maximum(np.abs(c) * 2.0 ** -4, 2.0 ** -10 * np.repeat(scales, 128, axis=1))
+    assert np.all(np.abs(cc - c) <= bound * (1 + 1e-6))
+    assert np.array_equal(kr, O.decode_bf16(rope))
+    # without RoPE input the RoPE bytes stay untouched (zero here)
+    assert np.all(O.quantise_latent_rows(c[:2], None)[:, 528:] == 0)
