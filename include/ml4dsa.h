@@ -36,7 +36,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 
-#define ML4_ABI_VERSION 1
+#define ML4_ABI_VERSION 2
 
 enum ml4_status {
   ML4_OK = 0,
@@ -215,6 +215,36 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
                           const void* q_mla, int32_t q_mla_dtype, int32_t* const* topk_bufs,
                           int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
                           void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream);
+
+/*
+ * ml4_index_cache_write / ml4_latent_cache_write -- quantise and pack new tokens into the
+ * paged caches the path reads (the step before it; a KV-sharing consumer layer calls
+ * neither).  [blog, ROCm implementation details › AITER 上的 DSA 索引器 (an FP8 indexer key
+ * with one scale per key, 132 B per token); › FP8 潜在缓存 (fp8_ds_mla: 512 FP8 values with
+ * four per-128 scales and 64 bf16 RoPE values, 656 B per token)]
+ *   Quantiser, per scale group (the whole 128-dim key; each 128 latent values):
+ *     scale = amax / 448,  code = E4M3(x / scale) rounded to nearest even and clamped to
+ *     +-448, in binary32; an all-zero group stores scale 0 and zero codes.
+ *   cache        ML4_IDX_FP8_132 (index) or ML4_LAT_FP8_656 (latent); rows are addressed
+ *                as pool + slot * row_bytes with 0 <= slot < num_blocks * block_size and
+ *                written through cache->pool (which these two entries treat as writable).
+ *   block_size   tokens per block (power of two, 16 .. 65536).
+ *   k / c        [n_tokens][128] / [n_tokens][512], BF16 or F32 (src_dtype).
+ *   k_rope       [n_tokens][64] bf16 with rope_dim 64; NULL with rope_dim 0 (NoPE: the RoPE
+ *                bytes of the row are left untouched).
+ *   slot_mapping [n_tokens] int64: destination slot = block_id * block_size + offset;
+ *                a negative slot skips that token (padding).
+ *   n_tokens     >= 0 (0: nothing is launched).
+ *   Device faults: a slot >= num_blocks * block_size sets ML4_FAULT_BLOCK_ID and skips
+ *   the token; a non-finite input value sets ML4_FAULT_RANGE (that row is unspecified).
+ */
+int ml4_index_cache_write(const ml4_cache* idx_cache, int32_t block_size, const void* k,
+                          int32_t src_dtype, int64_t n_tokens, const int64_t* slot_mapping,
+                          uint32_t* fault, hipStream_t stream);
+int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const void* c,
+                           int32_t src_dtype, const void* k_rope, int32_t rope_dim,
+                           int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
+                           hipStream_t stream);
 
 enum ml4_entry { ML4_ENTRY_TOPK = 1, ML4_ENTRY_MLA = 2, ML4_ENTRY_LAYER = 3 };
 

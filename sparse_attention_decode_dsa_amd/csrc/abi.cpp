@@ -376,6 +376,73 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
   return launch_status(ml4::launch_mla(ma, stream), "ml4_sparse_attn_layer");
 }
 
+namespace {
+
+int cache_write(const char* entry, bool latent, const ml4_cache* cache, int32_t block_size,
+                const void* src, int32_t src_dtype, const void* rope, int32_t rope_dim,
+                int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
+                hipStream_t stream) {
+  Checks c;
+  if (!cache) {
+    c.bad(true, latent ? "lat_cache is NULL" : "idx_cache is NULL");
+  } else {
+    c.bad(!cache->pool, "cache.pool is NULL");
+    c.bad(!aligned(cache->pool, 16), "cache.pool must be 16-byte aligned");
+    c.bad(cache->num_blocks < 1, "cache.num_blocks must be >= 1");
+    if (latent)
+      c.unsup(cache->format != ML4_LAT_FP8_656, "cache.format must be ML4_LAT_FP8_656");
+    else
+      c.unsup(cache->format != ML4_IDX_FP8_132, "cache.format must be ML4_IDX_FP8_132");
+  }
+  c.bad(!pow2(block_size), "block_size must be a power of two");
+  c.unsup(pow2(block_size) && (block_size < 16 || block_size > 65536),
+          "block_size outside 16 .. 65536");
+  c.bad(n_tokens < 0, "n_tokens must be >= 0");
+  c.unsup(src_dtype != ML4_BF16 && src_dtype != ML4_F32, "src_dtype must be ML4_BF16 or ML4_F32");
+  if (n_tokens > 0) {
+    c.bad(!src, "source values are NULL");
+    c.bad(!slot_mapping, "slot_mapping is NULL");
+    c.bad(!aligned(src, src_dtype == ML4_F32 ? 4 : 2), "source values misaligned");
+    c.bad(!aligned(slot_mapping, 8), "slot_mapping must be 8-byte aligned");
+  }
+  if (latent) {
+    c.unsup(rope_dim != 0 && rope_dim != ML4_ROPE_DIM, "rope_dim must be 0 or 64");
+    c.bad(rope_dim && n_tokens > 0 && (!rope || !aligned(rope, 8)),
+          "k_rope must be non-NULL and 8-byte aligned when rope_dim is 64");
+  }
+  c.unsup(n_tokens > ((int64_t)1 << 31), "n_tokens above 2^31");
+  if (int rc = c.finish(entry)) return rc;
+  ml4::CacheWriteLaunch a{};
+  a.latent = latent;
+  a.pool = const_cast<void*>(cache->pool);   // the write entries own the rows they write
+  a.capacity = cache->num_blocks * (int64_t)block_size;
+  a.src = src;
+  a.bf16 = src_dtype == ML4_BF16;
+  a.rope = rope_dim ? rope : nullptr;
+  a.rope_dim = rope_dim;
+  a.n_tokens = n_tokens;
+  a.slot_mapping = slot_mapping;
+  a.fault = fault;
+  return launch_status(ml4::launch_cache_write(a, stream), entry);
+}
+
+}  // namespace
+
+int ml4_index_cache_write(const ml4_cache* idx_cache, int32_t block_size, const void* k,
+                          int32_t src_dtype, int64_t n_tokens, const int64_t* slot_mapping,
+                          uint32_t* fault, hipStream_t stream) {
+  return cache_write("ml4_index_cache_write", false, idx_cache, block_size, k, src_dtype,
+                     nullptr, 0, n_tokens, slot_mapping, fault, stream);
+}
+
+int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const void* c,
+                           int32_t src_dtype, const void* k_rope, int32_t rope_dim,
+                           int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
+                           hipStream_t stream) {
+  return cache_write("ml4_latent_cache_write", true, lat_cache, block_size, c, src_dtype,
+                     k_rope, rope_dim, n_tokens, slot_mapping, fault, stream);
+}
+
 int ml4_fault_query(const uint32_t* fault, uint32_t* bits, hipStream_t stream) {
   if (!fault || !bits) {
     g_last_error = "ml4_fault_query: invalid: fault and bits must be non-NULL\n";

@@ -1,0 +1,123 @@
+// KV-cache writes on gfx950: quantise and pack new tokens into the 132-byte indexer rows and
+// the 656-byte fp8_ds_mla latent rows read by the rest of the path.
+//
+// Pages: "vLLM 首日支持 Mistral Large 4" (best2ai.com), ROCm implementation details ›
+// AITER 上的 DSA 索引器 (an FP8 indexer key with a single scale per key, 132 bytes per token)
+// and › FP8 潜在缓存 (fp8_ds_mla: 512 FP8 values with four scales, one per 128, and 64 bf16
+// RoPE values, 656 bytes per token).  The quantiser is the plain symmetric one: per scale
+// group scale = amax / 448 and code = E4M3(x / scale), round to nearest even, clamped to
+// +-448 (binary32 arithmetic); an all-zero group stores scale 0 and zero codes.
+//
+// One wave per token.  Index row: each lane converts two of the 128 values; the scale is a
+// wave-wide maximum.  Latent row: each lane converts eight of the 512 values, the 16 lanes of
+// a 128-value group reduce their maximum with xor shuffles, and lanes 0..15 copy the RoPE
+// bytes.  Both are streams: 256 B (bf16 key) or 1,160 B (bf16 latent + RoPE) read and 132 or
+// 656 B written per token.
+#include "ml4_device.h"
+
+namespace ml4 {
+
+namespace {
+
+constexpr int kIdxRowBytes = 132;
+constexpr int kLatRowBytes = 656;
+constexpr int kWavesPerWg = 4;
+constexpr float kE4m3Max = 448.0f;
+constexpr uint32_t kFaultSlot = 1u << 0;
+constexpr uint32_t kFaultRange = 1u << 4;
+
+__device__ __forceinline__ float load_value(const void* p, bool bf16, size_t i) {
+  return bf16 ? (float)static_cast<const __bf16*>(p)[i] : static_cast<const float*>(p)[i];
+}
+
+// Two binary32 values inside [-448, 448] -> two OCP E4M3 codes (round to nearest even) in
+// the low 16 bits.
+__device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float quantise_input(float x, float scale) {
+  if (scale == 0.f) return 0.f;
+  return fminf(fmaxf(x / scale, -kE4m3Max), kE4m3Max);
+}
+
+// Resolves the destination row of `token`; -1 = skip (negative slot: padding token).
+__device__ __forceinline__ int64_t dest_slot(const CacheWriteLaunch& a, int64_t token) {
+  const int64_t slot = a.slot_mapping[token];
+  if (slot < 0) return -1;
+  if (slot >= a.capacity) {
+    raise_fault(a.fault, kFaultSlot);
+    return -1;
+  }
+  return slot;
+}
+
+__global__ __launch_bounds__(kWavesPerWg * kWave) void k_index_write(CacheWriteLaunch a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;
+  const int64_t slot = dest_slot(a, token);
+  if (slot < 0) return;
+  const float x0 = load_value(a.src, a.bf16, token * 128 + 2 * lane);
+  const float x1 = load_value(a.src, a.bf16, token * 128 + 2 * lane + 1);
+  const bool finite = __builtin_isfinite(x0) && __builtin_isfinite(x1);
+  if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
+  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float scale = amax / kE4m3Max;
+  const uint32_t codes = to_e4m3x2(quantise_input(x0, scale), quantise_input(x1, scale));
+  uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kIdxRowBytes;
+  *reinterpret_cast<uint16_t*>(row + 2 * lane) = (uint16_t)codes;
+  if (lane == 0) *reinterpret_cast<float*>(row + 128) = scale;
+}
+
+__global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write(CacheWriteLaunch a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;
+  const int64_t slot = dest_slot(a, token);
+  if (slot < 0) return;
+  float x[8];
+  bool finite = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = load_value(a.src, a.bf16, token * 512 + 8 * lane + e);
+    finite &= __builtin_isfinite(x[e]);
+  }
+  if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  // maximum over the 16 lanes of this lane's 128-value group
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+  const float scale = m / kE4m3Max;
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = to_e4m3x2(quantise_input(x[4 * h], scale), quantise_input(x[4 * h + 1], scale));
+    const uint32_t hi = to_e4m3x2(quantise_input(x[4 * h + 2], scale), quantise_input(x[4 * h + 3], scale));
+    w[h] = lo | (hi << 16);
+  }
+  uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kLatRowBytes;
+  *reinterpret_cast<u32x2*>(row + 8 * lane) = u32x2{w[0], w[1]};
+  if ((lane & 15) == 0) *reinterpret_cast<float*>(row + 512 + 4 * (lane >> 4)) = scale;
+  if (a.rope_dim && lane < 16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.rope) +
+                                                     (size_t)token * 128 + 8 * lane);
+    *reinterpret_cast<uint2*>(row + 528 + 8 * lane) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteLaunch& a, hipStream_t st) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n_tokens + kWavesPerWg - 1) / kWavesPerWg));
+  if (a.latent)
+    k_latent_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
+  else
+    k_index_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ml4

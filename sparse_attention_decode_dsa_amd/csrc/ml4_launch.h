@@ -68,6 +68,20 @@ struct MlaLaunch {
 size_t mla_ws_bytes(const SeqView& s, int n_heads, int top_k);
 hipError_t launch_mla(const MlaLaunch& a, hipStream_t st);
 
+struct CacheWriteLaunch {
+  bool latent;          // 656-B fp8_ds_mla rows; else 132-B indexer rows
+  void* pool;
+  int64_t capacity;     // num_blocks * block_size rows
+  const void* src;      // [n_tokens][128 | 512]
+  bool bf16;            // src dtype bf16; else fp32
+  const void* rope;     // [n_tokens][64] bf16 (latent with rope_dim 64), else null
+  int rope_dim;
+  int64_t n_tokens;
+  const int64_t* slot_mapping;
+  uint32_t* fault;
+};
+hipError_t launch_cache_write(const CacheWriteLaunch& a, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace ml4

@@ -119,3 +119,24 @@ def test_layer_modes_are_validated():
 def test_fault_query_rejects_null():
     rc = M.LIB.ml4_fault_query(None, None, None)
     assert rc == M.ML4_E_INVALID
+
+
+def test_cache_write_default_deny_lists_every_reason():
+    """Host validation of the cache-write entries: every failed check listed, nothing
+    launched; zero tokens is a valid no-op."""
+    c = M.ml4_cache()
+    c.pool, c.num_blocks, c.format = 0, 0, M.ML4_IDX_F32      # fp32 rows are read-only
+    rc = M.ml4_index_cache_write(c, 48, None, 7, 5, None, None, stream=0, check=False)
+    msg = M.ml4_last_error()
+    assert rc == M.ML4_E_INVALID
+    for frag in ("cache.pool is NULL", "num_blocks", "block_size", "src_dtype",
+                 "source values are NULL", "slot_mapping is NULL", "ML4_IDX_FP8_132"):
+        assert frag in msg, (frag, msg)
+    c2 = M.ml4_cache()
+    c2.pool, c2.num_blocks, c2.format = 4096, 4, M.ML4_LAT_FP8_656
+    rc = M.ml4_latent_cache_write(c2, 64, None, M.ML4_BF16, None, 32, 0, None, None, stream=0,
+                                  check=False)
+    assert rc == M.ML4_E_UNSUPPORTED and "rope_dim" in M.ml4_last_error()
+    rc = M.ml4_latent_cache_write(c2, 64, None, M.ML4_BF16, None, 64, 0, None, None, stream=0,
+                                  check=False)
+    assert rc == M.ML4_OK
