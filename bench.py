@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB read + 1 GiB write streaming "
                          "kernel (counter calibration)")
+    ap.add_argument("--cache-write-tokens", type=int, default=65536,
+                    help="also time the KV-cache write entries on this many bf16 tokens "
+                         "(0 = skip); reported beside the step, not in it")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused entry instead (no per-kernel events)")
     return ap.parse_args()
@@ -154,6 +157,42 @@ def cpu_baseline(case, budget_s: float):
             "kind": "oracle",
             "sample": f"{rows_done} query rows ({len(sample)} whole requests), every layer of "
                       f"the step, fp64 numpy oracle; {elapsed:.1f} s of compute"}
+
+
+def time_cache_writes(n: int, dev: str, reps: int = 10):
+    """Quantise-and-pack of n new bf16 tokens into both caches (scattered slots).  Bytes per
+    token: index 128 x 2 in + 8 slot + 132 out; latent 512 x 2 + 64 x 2 in + 8 + 656 out."""
+    import torch
+
+    from sparse_attention_decode_dsa_amd import ml4dsa as M
+    g = torch.Generator(device=dev).manual_seed(1234)
+    bs = 64
+    nb = (n + bs - 1) // bs
+    k = torch.randn(n, 128, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.randn(n, 512, device=dev, generator=g).to(torch.bfloat16)
+    kr = torch.randn(n, 64, device=dev, generator=g).to(torch.bfloat16)
+    slots = torch.randperm(nb * bs, device=dev, generator=g)[:n].to(torch.int64)
+    ipool = torch.empty((nb, bs, 132), dtype=torch.uint8, device=dev)
+    lpool = torch.empty((nb, bs, 656), dtype=torch.uint8, device=dev)
+    fault = torch.zeros(1, dtype=torch.int32, device=dev)
+    ic, lc = M.make_cache(ipool, M.ML4_IDX_FP8_132), M.make_cache(lpool, M.ML4_LAT_FP8_656)
+    out = {"tokens": n}
+    for name, fn, per_tok in (
+            ("index", lambda: M.ml4_index_cache_write(ic, bs, k, M.ML4_BF16, n, slots, fault), 396),
+            ("latent", lambda: M.ml4_latent_cache_write(lc, bs, c, M.ML4_BF16, kr, 64, n, slots,
+                                                        fault), 1816)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        out[name] = {"us": us, "bytes": per_tok * n, "GBps": per_tok * n / (us * 1e-6) / 1e9}
+    assert M.ml4_fault_query(fault) == 0
+    return out
 
 
 def main():
@@ -277,6 +316,8 @@ def main():
         roof["avg_launch_us"] = us
         roof["traffic"] = load_traffic(dom)
         result["roofline"] = roof
+    if args.cache_write_tokens > 0:
+        result["cache_write"] = time_cache_writes(args.cache_write_tokens, dev)
     if args.cpu_seconds > 0:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

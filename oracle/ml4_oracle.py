@@ -49,6 +49,15 @@ Page titles used below:
    so it is decided in the kernel's precision: amax, the scale and x / scale are binary32
    operations (each correctly rounded), only the final E4M3 rounding is done here.
 
+7. Split-context merge  [blog, Long context › DCP (each context shard keeps its own top-2048
+   candidates; a stable top-k merge over (score, position) pairs -- the order of step 2 --
+   gives the row's top-k; partial attentions over disjoint key sets are merged through their
+   log-sum-exp)]:
+       merge:  top-k of the union of the shards' candidate lists, same order and output form
+               as step 2 (ascending position, -1 padded, length min(k, candidates));
+       LSE:    M = max_s lse_s,  o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M),
+               lse = M + ln sum_s e^(lse_s - M)  (shards with lse = -inf contribute nothing).
+
 Every step is the plain definition, in fp64, in the pages' order; numpy matrix products
 serve as the only library primitive.
 """
@@ -449,3 +458,44 @@ def quantise_latent_rows(c32: np.ndarray, rope_bf16_bits: Optional[np.ndarray]) 
             out[i, KV_LORA + 4 * ng:] = np.frombuffer(
                 np.asarray(rope_bf16_bits[i], dtype="<u2").tobytes(), dtype=np.uint8)
     return out
+
+
+# --------------------------------------------------------------------------------------
+# 7. Split-context merge  [blog, Long context › DCP]
+# --------------------------------------------------------------------------------------
+def topk_merge(cand_scores: np.ndarray, cand_pos: np.ndarray, cand_len: np.ndarray,
+               top_k: int) -> Tuple[np.ndarray, int]:
+    """cand_scores / cand_pos: [S][k_s] per-shard candidate lists (entries past cand_len[s]
+    are ignored); positions are distinct.  Top-k of their union in the order of step 2:
+    (idx[top_k] ascending, -1 padded; len)."""
+    sc, ps = [], []
+    for s_ in range(len(cand_len)):
+        n = int(cand_len[s_])
+        sc.append(np.asarray(cand_scores[s_][:n], dtype=np.float64))
+        ps.append(np.asarray(cand_pos[s_][:n], dtype=np.int64))
+    sc = np.concatenate(sc) if sc else np.zeros(0)
+    ps = np.concatenate(ps) if ps else np.zeros(0, dtype=np.int64)
+    assert len(np.unique(ps)) == len(ps)
+    nan = np.isnan(sc)
+    key = np.where(nan, 0.0, -sc)
+    order = np.lexsort((ps, key, nan))
+    n = min(top_k, len(ps))
+    out = np.full(top_k, -1, dtype=np.int64)
+    out[:n] = np.sort(ps[order[:n]])
+    return out, n
+
+
+def lse_combine(o_parts: np.ndarray, lse_parts: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """o_parts [S][H][D], lse_parts [S][H] (natural log; -inf = empty shard) ->
+    (o [H][D], lse [H])."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    M = np.max(lse_parts, axis=0)
+    live = np.isfinite(M)
+    Ms = np.where(live, M, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Ms[None, :]), 0.0)
+    den = w.sum(axis=0)
+    o = np.einsum("sh,shd->hd", w, o_parts) / np.where(den > 0, den, 1.0)[:, None]
+    o[~live] = 0.0
+    lse = np.where(live, Ms + np.log(np.where(den > 0, den, 1.0)), -np.inf)
+    return o, lse

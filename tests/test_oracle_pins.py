@@ -459,3 +459,62 @@ def test_latent_row_quantiser_groups_rope_and_reader_round_trip():
     assert np.array_equal(kr, O.decode_bf16(rope))
     # without RoPE input the RoPE bytes stay untouched (zero here)
     assert np.all(O.quantise_latent_rows(c[:2], None)[:, 528:] == 0)
+
+
+# ---------------------------------------------------------------- split-context merge
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_merge_of_chunk_topks_equals_row_topk(seed):
+    """Top-k of the union of per-chunk top-k lists is the row's top-k (every key of the
+    row's top-k is in its chunk's top-k), with duplicates, -0, -inf and NaN in the row."""
+    g = np.random.default_rng(seed)
+    n = int(g.integers(50, 400))
+    k = int(g.integers(1, 40))
+    x = np.round(g.standard_normal(n) * 3) / 3
+    x[g.integers(0, n, 5)] = -0.0
+    x[g.integers(0, n, 3)] = -np.inf
+    x[g.integers(0, n, 2)] = np.nan
+    S = int(g.integers(1, 9))
+    bounds = np.linspace(0, n, S + 1).astype(int)
+    cs, cp, cl = np.zeros((S, k)), np.full((S, k), -1), np.zeros(S, dtype=int)
+    for s_ in range(S):
+        lo, hi = bounds[s_], bounds[s_ + 1]
+        if hi > lo:
+            idx, ln = O.topk_row(x[lo:hi], hi - lo - 1, k)
+            cs[s_, :ln], cp[s_, :ln], cl[s_] = x[lo + idx[:ln]], lo + idx[:ln], ln
+    got, gl = O.topk_merge(cs, cp, cl, k)
+    want, wl = O.topk_row(x, n - 1, k)
+    assert gl == wl and np.array_equal(got, want)
+
+
+def test_topk_merge_brute_force_order():
+    cs = np.array([[3.0, 1.0, 0.0], [3.0, 2.0, -0.0]])
+    cp = np.array([[7, 2, 5], [4, 9, 1]])
+    got, n = O.topk_merge(cs, cp, np.array([3, 3]), 4)
+    # 3.0@4 and 3.0@7 (tie: lower position first), 2.0@9, 1.0@2 -> ascending positions
+    assert n == 4 and list(got) == [2, 4, 7, 9]
+    got, n = O.topk_merge(cs, cp, np.array([1, 0]), 4)
+    assert n == 1 and list(got) == [7, -1, -1, -1]
+
+
+def test_lse_combine_of_split_attention_equals_full_attention():
+    """Attention over disjoint key subsets, merged by LSE, equals attention over all keys
+    (torch float64 softmax as the independent reference)."""
+    g = torch.Generator().manual_seed(4)
+    H, D, n, S = 6, 16, 50, 4
+    q = torch.randn(H, D, generator=g, dtype=torch.float64)
+    kv = torch.randn(n, D, generator=g, dtype=torch.float64)
+    logits = q @ kv.T * 0.7
+    full = torch.softmax(logits, dim=1) @ kv
+    full_lse = torch.logsumexp(logits, dim=1)
+    parts = torch.randperm(n, generator=g).chunk(S - 1)
+    o_parts, lse_parts = [], []
+    for p in parts:
+        l = logits[:, p]
+        o_parts.append((torch.softmax(l, dim=1) @ kv[p]).numpy())
+        lse_parts.append(torch.logsumexp(l, dim=1).numpy())
+    o_parts.append(np.zeros((H, D)))                 # an empty shard
+    lse_parts.append(np.full(H, -np.inf))
+    o, lse = O.lse_combine(np.stack(o_parts), np.stack(lse_parts))
+    assert np.allclose(o, full.numpy(), atol=1e-12) and np.allclose(lse, full_lse.numpy())
+    o, lse = O.lse_combine(np.zeros((2, H, D)), np.full((2, H), -np.inf))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
