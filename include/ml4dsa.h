@@ -246,6 +246,35 @@ int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const
                            int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
                            hipStream_t stream);
 
+/*
+ * ml4_topk_merge -- exact top-k over the union of per-shard candidate lists, for context
+ * split across shards (devices or chunks of one long row).  [blog, Long context › DCP (each
+ * shard keeps its own top-2048; a stable top-k merge over (score, position) pairs; radix
+ * select over packed candidates)]
+ *   cand_scores [rows][n_shards][ld_cand] fp32, cand_pos [rows][n_shards][ld_cand] int32
+ *   (distinct positions >= 0 within a row), cand_len [rows][n_shards] (entries past it are
+ *   ignored).  n_shards * ld_cand <= 16384, 1 <= top_k <= 2048.
+ *   Order as ml4_topk_select (score descending, -0 == +0, NaN lowest and reported, equal
+ *   scores lower position first); output ascending positions, -1 padded, topk_len =
+ *   min(top_k, number of candidates).  A length outside [0, ld_cand] or a negative
+ *   position sets ML4_FAULT_TOPK_INDEX (the entry is skipped).
+ *
+ * ml4_lse_combine -- merge partial attentions over disjoint key sets by their log-sum-exp.
+ *   [blog, Long context › DCP (partial outputs merged through their LSE)]
+ *   o_parts [rows][n_shards][n_heads][head_dim] fp32, lse_parts [rows][n_shards][n_heads]
+ *   (natural log; -inf = the shard saw no key): out[r][h] = sum_s e^(lse_s - M) o_s /
+ *   sum_s e^(lse_s - M), lse = M + ln sum_s e^(lse_s - M), M = max_s lse_s (out 0 and lse
+ *   -inf when every shard is empty).  out [rows][n_heads][head_dim] BF16 or F32; lse
+ *   [rows][n_heads] fp32 or NULL.  head_dim 1 .. 4096.
+ */
+int ml4_topk_merge(int32_t rows, int32_t n_shards, const float* cand_scores,
+                   const int32_t* cand_pos, const int32_t* cand_len, int64_t ld_cand,
+                   int32_t top_k, int32_t* topk_idx, int32_t* topk_len, uint32_t* fault,
+                   hipStream_t stream);
+int ml4_lse_combine(int32_t rows, int32_t n_heads, int32_t n_shards, int32_t head_dim,
+                    const float* o_parts, const float* lse_parts, void* out, int32_t out_dtype,
+                    float* lse, hipStream_t stream);
+
 enum ml4_entry { ML4_ENTRY_TOPK = 1, ML4_ENTRY_MLA = 2, ML4_ENTRY_LAYER = 3 };
 
 /* Workspace bytes an entry point needs for this batch (256-B aligned start required).

@@ -443,6 +443,68 @@ int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const
                      k_rope, rope_dim, n_tokens, slot_mapping, fault, stream);
 }
 
+int ml4_topk_merge(int32_t rows, int32_t n_shards, const float* cand_scores,
+                   const int32_t* cand_pos, const int32_t* cand_len, int64_t ld_cand,
+                   int32_t top_k, int32_t* topk_idx, int32_t* topk_len, uint32_t* fault,
+                   hipStream_t stream) {
+  Checks c;
+  c.bad(rows < 0, "rows must be >= 0");
+  c.bad(n_shards < 1, "n_shards must be >= 1");
+  c.bad(ld_cand < 1, "ld_cand must be >= 1");
+  c.unsup(n_shards >= 1 && ld_cand >= 1 && (int64_t)n_shards * ld_cand > 16384,
+          "n_shards * ld_cand above 16384");
+  c.bad(top_k < 1 || top_k > ML4_MAX_TOPK, "top_k must be in 1 .. 2048");
+  if (rows > 0) {
+    c.bad(!cand_scores || !cand_pos || !cand_len, "candidate arrays must be non-NULL");
+    c.bad(!topk_idx || !topk_len, "topk_idx and topk_len must be non-NULL");
+    c.bad(!aligned(cand_scores, 4) || !aligned(cand_pos, 4) || !aligned(cand_len, 4) ||
+              !aligned(topk_idx, 4) || !aligned(topk_len, 4),
+          "arrays must be 4-byte aligned");
+  }
+  if (int rc = c.finish("ml4_topk_merge")) return rc;
+  ml4::MergeLaunch a{};
+  a.rows = rows;
+  a.n_shards = n_shards;
+  a.ld = ld_cand;
+  a.cand_scores = cand_scores;
+  a.cand_pos = cand_pos;
+  a.cand_len = cand_len;
+  a.top_k = top_k;
+  a.idx = topk_idx;
+  a.len = topk_len;
+  a.fault = fault;
+  return launch_status(ml4::launch_topk_merge(a, stream), "ml4_topk_merge");
+}
+
+int ml4_lse_combine(int32_t rows, int32_t n_heads, int32_t n_shards, int32_t head_dim,
+                    const float* o_parts, const float* lse_parts, void* out, int32_t out_dtype,
+                    float* lse, hipStream_t stream) {
+  Checks c;
+  c.bad(rows < 0, "rows must be >= 0");
+  c.bad(n_heads < 1 || n_heads > 65535, "n_heads must be in 1 .. 65535");
+  c.bad(n_shards < 1, "n_shards must be >= 1");
+  c.bad(head_dim < 1 || head_dim > 4096, "head_dim must be in 1 .. 4096");
+  c.unsup(out_dtype != ML4_BF16 && out_dtype != ML4_F32, "out_dtype must be ML4_BF16 or ML4_F32");
+  if (rows > 0) {
+    c.bad(!o_parts || !lse_parts || !out, "o_parts, lse_parts and out must be non-NULL");
+    c.bad(!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(lse, 4) ||
+              !aligned(out, out_dtype == ML4_F32 ? 4 : 2),
+          "arrays misaligned");
+  }
+  if (int rc = c.finish("ml4_lse_combine")) return rc;
+  ml4::LseCombineLaunch a{};
+  a.rows = rows;
+  a.n_heads = n_heads;
+  a.n_shards = n_shards;
+  a.head_dim = head_dim;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.out = out;
+  a.out_bf16 = out_dtype == ML4_BF16;
+  a.lse = lse;
+  return launch_status(ml4::launch_lse_combine(a, stream), "ml4_lse_combine");
+}
+
 int ml4_fault_query(const uint32_t* fault, uint32_t* bits, hipStream_t stream) {
   if (!fault || !bits) {
     g_last_error = "ml4_fault_query: invalid: fault and bits must be non-NULL\n";

@@ -82,6 +82,29 @@ struct CacheWriteLaunch {
 };
 hipError_t launch_cache_write(const CacheWriteLaunch& a, hipStream_t st);
 
+struct MergeLaunch {
+  int rows, n_shards;
+  int64_t ld;                 // entries per shard list
+  const float* cand_scores;   // [rows][n_shards][ld]
+  const int32_t* cand_pos;    // [rows][n_shards][ld]
+  const int32_t* cand_len;    // [rows][n_shards]
+  int top_k;
+  int32_t* idx;
+  int32_t* len;
+  uint32_t* fault;
+};
+hipError_t launch_topk_merge(const MergeLaunch& a, hipStream_t st);
+
+struct LseCombineLaunch {
+  int rows, n_heads, n_shards, head_dim;
+  const float* o_parts;       // [rows][n_shards][n_heads][head_dim]
+  const float* lse_parts;     // [rows][n_shards][n_heads], natural log
+  void* out;                  // [rows][n_heads][head_dim]
+  bool out_bf16;
+  float* lse;                 // [rows][n_heads] or null
+};
+hipError_t launch_lse_combine(const LseCombineLaunch& a, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace ml4

@@ -28,7 +28,8 @@ ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
            "ml4_sparse_attn_layer", "ml4_index_cache_write", "ml4_latent_cache_write",
-           "ml4_workspace_bytes", "ml4_last_error", "ml4_fault_query", "ml4_abi_version")
+           "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
+           "ml4_fault_query", "ml4_abi_version")
 
 
 class ml4_seqs(C.Structure):
@@ -92,6 +93,10 @@ def _load() -> C.CDLL:
     lib.ml4_latent_cache_write.restype = C.c_int
     lib.ml4_latent_cache_write.argtypes = [P(ml4_cache), i32, vp, i32, vp, i32, i64, vp, vp,
                                            vp]
+    lib.ml4_topk_merge.restype = C.c_int
+    lib.ml4_topk_merge.argtypes = [i32, i32, vp, vp, vp, i64, i32, vp, vp, vp, vp]
+    lib.ml4_lse_combine.restype = C.c_int
+    lib.ml4_lse_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     if lib.ml4_abi_version() != ML4_ABI_VERSION:
         raise ImportError("libml4dsa.so ABI version mismatch")
     return lib
@@ -226,4 +231,19 @@ def ml4_latent_cache_write(lat_cache, block_size, c, src_dtype, k_rope, rope_dim
     rc = LIB.ml4_latent_cache_write(C.byref(lat_cache), block_size, ptr(c), src_dtype,
                                     ptr(k_rope), rope_dim, n_tokens, ptr(slot_mapping),
                                     ptr(fault), stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_topk_merge(rows, n_shards, cand_scores, cand_pos, cand_len, ld_cand, top_k, topk_idx,
+                   topk_len, fault=None, stream=None, check=True) -> int:
+    rc = LIB.ml4_topk_merge(rows, n_shards, ptr(cand_scores), ptr(cand_pos), ptr(cand_len),
+                            ld_cand, top_k, ptr(topk_idx), ptr(topk_len), ptr(fault),
+                            stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_lse_combine(rows, n_heads, n_shards, head_dim, o_parts, lse_parts, out, out_dtype,
+                    lse=None, stream=None, check=True) -> int:
+    rc = LIB.ml4_lse_combine(rows, n_heads, n_shards, head_dim, ptr(o_parts), ptr(lse_parts),
+                             ptr(out), out_dtype, ptr(lse), stream_handle(stream))
     return _check(rc) if check else rc
