@@ -196,6 +196,29 @@ def latent_rows_f32(pool: np.ndarray, s: np.ndarray, rope_dim: int
     return flat[:, :KV_LORA], flat[:, KV_LORA:KV_LORA + rope_dim]
 
 
+def latent_rows_bf16(pool: np.ndarray, s: np.ndarray, rope_dim: int
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """pool: uint16 bf16 bits [num_blocks, block_size, 576] (512 latent then 64 RoPE) -- the
+    uncompressed 1,152-B row [blog, "FP8 潜在缓存"].  With rope_dim == 0 the RoPE values are
+    never read."""
+    flat = pool.reshape(-1, KV_LORA + ROPE_DIM)[s]
+    return decode_bf16(flat[:, :KV_LORA]), decode_bf16(flat[:, KV_LORA:KV_LORA + rope_dim])
+
+
+def window_positions(q_pos: np.ndarray, window: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Sliding-window selection [blog, Long context (DSpark draft layers: a 2,048-token
+    window)]: row r attends to max(0, p_r - window + 1) .. p_r.  Returned in the top-k list
+    form (idx [rows][window] ascending, -1 padded; len)."""
+    idx = np.full((len(q_pos), window), -1, dtype=np.int64)
+    ln = np.zeros(len(q_pos), dtype=np.int64)
+    for r, p in enumerate(q_pos):
+        lo = max(0, int(p) - window + 1)
+        n = int(p) - lo + 1
+        idx[r, :n] = np.arange(lo, int(p) + 1)
+        ln[r] = n
+    return idx, ln
+
+
 def ssmax_multiplier(ssmax_s: float, pos: int) -> float:
     """SSMax logit multiplier s * ln(n) with n = p + 1 visible keys; 1 when s <= 0."""
     return ssmax_s * math.log(pos + 1) if ssmax_s > 0 else 1.0
@@ -270,6 +293,7 @@ def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: 
     """o [len(rows), H, 512] and lse [len(rows), H] in fp64.
 
     fmt 'fp8': pool uint8 [nb, bs, 656]; q uint16 bf16 bits [total_q, H, 512 + rope_dim].
+    fmt 'bf16': pool uint16 bf16 bits [nb, bs, 576]; q as for 'fp8'.
     fmt 'f32': pool float32 [nb, bs, 576]; q float32 [total_q, H, 512 + rope_dim].
     topk_idx holds logical positions; entries past topk_len[r] are ignored.
     """
@@ -286,6 +310,9 @@ def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: 
         s = slots(seqs, b, t)
         if fmt == "fp8":
             c, kr = latent_rows_fp8(pool, s, rope_dim)
+            qv = decode_bf16(q[r])
+        elif fmt == "bf16":
+            c, kr = latent_rows_bf16(pool, s, rope_dim)
             qv = decode_bf16(q[r])
         else:
             c, kr = latent_rows_f32(pool, s, rope_dim)
@@ -311,13 +338,13 @@ def dense_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: i
     H = q.shape[1]
     o = np.zeros((len(rows), H, KV_LORA))
     lse = np.zeros((len(rows), H))
-    dec = latent_rows_fp8 if fmt == "fp8" else latent_rows_f32
+    dec = {"fp8": latent_rows_fp8, "bf16": latent_rows_bf16}.get(fmt, latent_rows_f32)
     for i, r in enumerate(rows):
         b = seqs.request_of(r)
         p = int(seqs.q_pos[r])
         c, kr = dec(pool, slots(seqs, b, np.arange(p + 1)), rope_dim)
         K = np.concatenate([c, kr], axis=1)               # [n, 512 + rope]
-        qv = decode_bf16(q[r]) if fmt == "fp8" else np.asarray(q[r], np.float64)
+        qv = decode_bf16(q[r]) if fmt in ("fp8", "bf16") else np.asarray(q[r], np.float64)
         Q = qv[:, :KV_LORA + rope_dim]
         S = softmax_scale * ssmax_multiplier(ssmax_s, p) * (Q @ K.T)
         mx = S.max(axis=1)

@@ -151,6 +151,12 @@ def make_latent_pool(seed: int, num_blocks: int, block_size: int, fmt: str,
     if fmt == "f32":
         return torch.randn((num_blocks, block_size, KV_LORA + ROPE_DIM), generator=g,
                            device=device)
+    if fmt == "bf16":      # the uncompressed 1,152-byte row: 576 bf16 values
+        x = torch.randn((num_blocks, block_size, KV_LORA + ROPE_DIM), generator=g,
+                        device=device).to(torch.bfloat16)
+        if nan_rope:
+            x[..., KV_LORA:] = float("nan")
+        return x
     row = KV_LORA + 4 * (KV_LORA // 128) + 2 * ROPE_DIM
     out = torch.empty((ntok, row), dtype=torch.uint8, device=device)
     for s in range(0, ntok, chunk_tokens):

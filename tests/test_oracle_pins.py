@@ -518,3 +518,23 @@ def test_lse_combine_of_split_attention_equals_full_attention():
     assert np.allclose(o, full.numpy(), atol=1e-12) and np.allclose(lse, full_lse.numpy())
     o, lse = O.lse_combine(np.zeros((2, H, D)), np.full((2, H), -np.inf))
     assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------- bf16 rows, sliding window
+def test_bf16_rows_and_window_selection_reduce_to_dense_attention():
+    """bf16 latent rows read back as their values; a window covering the whole context is
+    dense attention; the window positions are the trailing ones, clipped at 0."""
+    g = torch.Generator().manual_seed(9)
+    rows = torch.randn(1, 16, 576, generator=g).to(torch.bfloat16)
+    bits = P.bf16_bits(rows.float())
+    seqs = O.Seqs(np.array([16]), np.array([0, 2]), np.array([9, 15]), np.arange(1)[None, :], 16)
+    c, kr = O.latent_rows_bf16(bits, np.arange(16), 64)
+    assert np.array_equal(c, rows.float().numpy()[0, :, :512].astype(np.float64))
+    assert np.array_equal(kr, rows.float().numpy()[0, :, 512:].astype(np.float64))
+    idx, ln = O.window_positions(np.array([9, 15, 2]), 4)
+    assert list(idx[0]) == [6, 7, 8, 9] and list(idx[2]) == [0, 1, 2, -1] and list(ln) == [4, 4, 3]
+    q = P.bf16_bits(torch.randn(2, 4, 576, generator=g))
+    widx, wln = O.window_positions(seqs.q_pos, 64)
+    o, lse = O.sparse_mla(seqs, bits, "bf16", q, 64, widx, wln, 0.05, 0.0)
+    od, lsed = O.dense_mla(seqs, bits, "bf16", q, 64, 0.05, 0.0)
+    assert np.allclose(o, od, atol=1e-12) and np.allclose(lse, lsed)
