@@ -61,7 +61,9 @@ enum ml4_index_format {
  * layer)]; KV LoRA rank 512 and RoPE dim 64 [blog, Highlights]. */
 enum ml4_latent_format {
   ML4_LAT_F32 = 0,      /* [512 x fp32 latent][64 x fp32 RoPE] = 2,304 B (fp32 test format) */
-  ML4_LAT_FP8_656 = 1   /* [512 x e4m3][4 x fp32 scale, one per 128][64 x bf16 RoPE] = 656 B */
+  ML4_LAT_FP8_656 = 1,  /* [512 x e4m3][4 x fp32 scale, one per 128][64 x bf16 RoPE] = 656 B */
+  ML4_LAT_BF16_1152 = 2 /* [512 x bf16][64 x bf16 RoPE] = 1,152 B ([blog] FP8 潜在缓存: the
+                           uncompressed bf16 row the FP8 layouts are measured against)     */
 };
 
 #define ML4_IDX_DIM 128
@@ -171,6 +173,22 @@ int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, i
 int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
                           int32_t q_dtype, int32_t n_heads, int32_t rope_dim,
                           const int32_t* topk_idx, const int32_t* topk_len, int32_t top_k,
+                          float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
+                          float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
+                          hipStream_t stream);
+
+/*
+ * ml4_window_mla_decode -- MLA over the last `window` positions of each row (a sliding
+ * window, no indexer), on the same kernel.  [blog, Long context (DSpark draft layers attend
+ * to a 2,048-token sliding window over a bf16 KV cache)]
+ *   Row r attends to positions max(0, q_pos[r] - window + 1) .. q_pos[r] with the formula of
+ *   ml4_sparse_mla_decode.  kv: ML4_LAT_BF16_1152 or ML4_LAT_FP8_656.  1 <= window <= 2048.
+ *   ws: ml4_workspace_bytes(ML4_ENTRY_MLA, s, n_heads, window) bytes.
+ *   With ML4_LAT_BF16_1152 the latent values must lie within the fp16 range (PV runs on
+ *   fp16 MFMA); QK and the RoPE part run on bf16 MFMA with the query as given.
+ */
+int ml4_window_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
+                          int32_t q_dtype, int32_t n_heads, int32_t rope_dim, int32_t window,
                           float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
                           float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
                           hipStream_t stream);

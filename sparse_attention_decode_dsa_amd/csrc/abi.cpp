@@ -6,6 +6,7 @@
 // deployments at start-up with an error that lists every reason].
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -91,7 +92,8 @@ void check_cache(Checks& c, const ml4_cache* k, bool index, const char* name) {
   if (k->num_blocks < 1) c.invalid.push_back(n + ".num_blocks must be >= 1");
   if (index && k->format != ML4_IDX_F32 && k->format != ML4_IDX_FP8_132)
     c.invalid.push_back(n + ".format is not an ml4_index_format");
-  if (!index && k->format != ML4_LAT_F32 && k->format != ML4_LAT_FP8_656)
+  if (!index && k->format != ML4_LAT_F32 && k->format != ML4_LAT_FP8_656 &&
+      k->format != ML4_LAT_BF16_1152)
     c.invalid.push_back(n + ".format is not an ml4_latent_format");
 }
 
@@ -145,22 +147,26 @@ void check_topk(Checks& c, int32_t top_k, const int32_t* idx, const int32_t* len
 
 void check_mla(Checks& c, const ml4_cache* kv, const void* q, int32_t q_dtype, int32_t n_heads,
                int32_t rope_dim, const int32_t* idx, const int32_t* len, int32_t top_k,
-               float softmax_scale, float ssmax_s, const void* out, int32_t out_dtype) {
+               float softmax_scale, float ssmax_s, const void* out, int32_t out_dtype,
+               int32_t window = 0) {
   check_cache(c, kv, false, "kv");
   c.bad(!q, "q is NULL");
   c.bad(!aligned(q, 16), "q must be 16-byte aligned");
   if (kv) {
-    c.bad(kv->format == ML4_LAT_FP8_656 && q_dtype != ML4_BF16,
-          "an ML4_LAT_FP8_656 cache needs ML4_BF16 queries");
-    c.bad(kv->format == ML4_LAT_FP8_656 && out_dtype != ML4_BF16,
-          "an ML4_LAT_FP8_656 cache writes ML4_BF16 outputs");
+    const bool rows16 = kv->format == ML4_LAT_FP8_656 || kv->format == ML4_LAT_BF16_1152;
+    c.bad(rows16 && q_dtype != ML4_BF16,
+          "an ML4_LAT_FP8_656 / ML4_LAT_BF16_1152 cache needs ML4_BF16 queries");
+    c.bad(rows16 && out_dtype != ML4_BF16,
+          "an ML4_LAT_FP8_656 / ML4_LAT_BF16_1152 cache writes ML4_BF16 outputs");
     c.bad(kv->format == ML4_LAT_F32 && (q_dtype != ML4_F32 || out_dtype != ML4_F32),
           "an ML4_LAT_F32 cache needs ML4_F32 queries and outputs");
   }
   c.unsup(n_heads < 16 || n_heads > 128 || n_heads % 16 != 0,
           "n_heads must be a multiple of 16 in 16 .. 128");
   c.unsup(rope_dim != 0 && rope_dim != ML4_ROPE_DIM, "rope_dim must be 64 or 0 (NoPE)");
-  c.bad(!idx || !len, "topk_idx and topk_len must be non-NULL");
+  c.bad(window == 0 && (!idx || !len), "topk_idx and topk_len must be non-NULL");
+  c.unsup(window > 0 && kv && kv->format == ML4_LAT_F32,
+          "window attention needs an ML4_LAT_FP8_656 or ML4_LAT_BF16_1152 cache");
   c.bad(top_k < 1, "top_k must be >= 1");
   c.unsup(top_k > ML4_MAX_TOPK, "top_k above 2048");
   c.bad(!(softmax_scale > 0.f) || !std::isfinite(softmax_scale),
@@ -261,7 +267,8 @@ int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   a.s = view(s);
   a.pool = kv->pool;
   a.num_blocks = kv->num_blocks;
-  a.fp8 = kv->format == ML4_LAT_FP8_656;
+  a.fp8 = kv->format != ML4_LAT_F32;
+  a.bf16_rows = kv->format == ML4_LAT_BF16_1152;
   a.q = q;
   a.n_heads = n_heads;
   a.rope_dim = rope_dim;
@@ -275,6 +282,42 @@ int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   a.ws = ws;
   a.fault = fault;
   return launch_status(ml4::launch_mla(a, stream), "ml4_sparse_mla_decode");
+}
+
+int ml4_window_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
+                          int32_t q_dtype, int32_t n_heads, int32_t rope_dim, int32_t window,
+                          float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
+                          float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
+                          hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  c.bad(window < 1, "window must be >= 1");
+  check_mla(c, kv, q, q_dtype, n_heads, rope_dim, nullptr, nullptr, std::max(window, 1),
+            softmax_scale, ssmax_s, out, out_dtype, std::max(window, 1));
+  if (c.invalid.empty() && c.unsupported.empty()) {
+    const size_t need = ml4_workspace_bytes(ML4_ENTRY_MLA, s, n_heads, window);
+    c.ws(ws_bytes < need, bytes_msg("window-MLA workspace", need, ws_bytes));
+    c.ws(need && (!ws || !aligned(ws, 256)), "workspace must be non-NULL and 256-byte aligned");
+  }
+  if (int rc = c.finish("ml4_window_mla_decode")) return rc;
+  ml4::MlaLaunch a{};
+  a.s = view(s);
+  a.pool = kv->pool;
+  a.num_blocks = kv->num_blocks;
+  a.fp8 = true;
+  a.bf16_rows = kv->format == ML4_LAT_BF16_1152;
+  a.window = window;
+  a.q = q;
+  a.n_heads = n_heads;
+  a.rope_dim = rope_dim;
+  a.top_k = window;
+  a.softmax_scale = softmax_scale;
+  a.ssmax_s = ssmax_s;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.fault = fault;
+  return launch_status(ml4::launch_mla(a, stream), "ml4_window_mla_decode");
 }
 
 int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache* lat_caches,
@@ -360,7 +403,8 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
   ma.s = v;
   ma.pool = lat_caches[lat_layer].pool;
   ma.num_blocks = lat_caches[lat_layer].num_blocks;
-  ma.fp8 = lat_caches[lat_layer].format == ML4_LAT_FP8_656;
+  ma.fp8 = lat_caches[lat_layer].format != ML4_LAT_F32;
+  ma.bf16_rows = lat_caches[lat_layer].format == ML4_LAT_BF16_1152;
   ma.q = q_mla;
   ma.n_heads = L->mla_heads;
   ma.rope_dim = L->rope_dim;

@@ -51,7 +51,9 @@ struct MlaLaunch {
   SeqView s;
   const void* pool;
   int64_t num_blocks;
-  bool fp8;             // ML4_LAT_FP8_656 + bf16 q/out; else ML4_LAT_F32 + fp32 q/out
+  bool fp8;             // ML4_LAT_FP8_656 / ML4_LAT_BF16_1152 + bf16 q/out; else ML4_LAT_F32
+  bool bf16_rows;       // ML4_LAT_BF16_1152
+  int window;           // > 0: attend to the last `window` positions (idx / len unused)
   const void* q;
   int n_heads;
   int rope_dim;

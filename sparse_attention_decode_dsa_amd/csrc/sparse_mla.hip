@@ -37,7 +37,6 @@ namespace ml4 {
 
 namespace {
 
-constexpr int kLatRow = 656;
 constexpr int kTK = 32;            // keys per tile
 constexpr int kQRS = 72;           // bf16 stride of a head's RoPE query in LDS (64 + 8)
 constexpr float kRescaleSlack = 8.0f;
@@ -98,21 +97,32 @@ __device__ __forceinline__ float sum_over_lane_groups(float v) {
 // (one transfer instruction each); instructions past the tile write a junk block.  The
 // tile's rows sit at a stride of RS = 16 NCH bytes with the cache row's own layout, and the
 // matrix-core operands are read from there directly.
-template <int ROPE>
+//   FMT kFmtFp8:  fp8_ds_mla rows, [512 e4m3][4 x fp32 scale][64 x bf16 RoPE] = 656 B;
+//   FMT kFmtBf16: bf16 rows, [512 x bf16][64 x bf16 RoPE] = 1,152 B (four-tile ring does not
+//                 fit; two tiles, one in flight).
+constexpr int kFmtFp8 = 0, kFmtBf16 = 1;
+
+template <int ROPE, int FMT>
 struct MlaGeom {
-  static constexpr int NCH = ROPE ? 41 : 33;            // 16-byte chunks read per row
+  static constexpr int ROW_BYTES = FMT == kFmtFp8 ? 656 : 1152;     // cache row stride
+  static constexpr int ROPE_OFF = FMT == kFmtFp8 ? 528 : 1024;
+  static constexpr int NCH = (ROPE ? ROW_BYTES : ROPE_OFF) / 16;   // 16-B chunks read per row
+  static constexpr int NSTAGE = FMT == kFmtFp8 ? kNStage : 2;
   static constexpr int RS = 16 * NCH;                   // bytes per gathered row
   static constexpr int RAW = kTK * NCH;                 // chunks per tile
   static constexpr int NBLK = (RAW + kWave - 1) / kWave;
   static constexpr int PER_WAVE = (NBLK + kMlaWaves - 1) / kMlaWaves;
   static constexpr int STAGE = NBLK * 1024;
-  static constexpr int OFF_JUNK = kNStage * STAGE;
+  static constexpr int OFF_JUNK = NSTAGE * STAGE;
   static constexpr int OFF_XS = OFF_JUNK + 1024;                      // [8][4][64] f32x4
   static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] bf16
   static constexpr int OFF_SLOT = OFF_QR + (ROPE ? kHeadsPerWg * kQRS * 2 : 0);
   static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
 };
-static_assert(MlaGeom<64>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<64, kFmtFp8>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<64, kFmtBf16>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<0, kFmtFp8>::RS == 528 && MlaGeom<64, kFmtFp8>::RS == 656, "rows");
+static_assert(MlaGeom<0, kFmtBf16>::RS == 1024 && MlaGeom<64, kFmtBf16>::RS == 1152, "rows");
 
 // Work split inside a work-group of 8 waves (one query row, up to 128 heads): wave w owns
 // head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half dh = w >> 2
@@ -120,20 +130,46 @@ static_assert(MlaGeom<64>::BYTES <= 160 * 1024, "LDS budget");
 // fragment read from LDS feeds two MFMAs.  Per wave the latent query takes 64 registers and
 // the output accumulator 128; the RoPE query is read from LDS per tile.
 
-// Latent bytes of a gathered row: [512 e4m3][4 x fp32 scale][64 x bf16 RoPE].
+constexpr int kQkAhead = 2;   // bf16 K fragments in flight ahead of the MFMAs
+
+// Scale offset of an fp8_ds_mla row.
 constexpr int kScaleOff = 512;
-constexpr int kRopeOff = 528;
+
+// Query-fragment register type: fp16 for the e4m3 rows (decoded exactly to fp16), bf16 as
+// given for the bf16 rows.
+template <int FMT> struct QFrag { typedef f16x8 type; };
+template <> struct QFrag<kFmtBf16> { typedef bf16x8 type; };
+
+// Eight bf16 values (four per 64-bit half) -> fp16, exactly for |x| in [2^-14, 65504]
+// (8 significant bits fit in 11): the bf16 bits shifted up are the binary32 value, and the
+// truncating pack loses nothing.
+__device__ __forceinline__ f16x8 bf16x8_to_f16(const s16x4& lo, const s16x4& hi) {
+  f16x8 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const s16x4& v = h ? hi : lo;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float a = __uint_as_float((uint32_t)(uint16_t)v[e] << 16);
+      const float b = __uint_as_float((uint32_t)(uint16_t)v[e + 1] << 16);
+      const auto pk = __builtin_amdgcn_cvt_pkrtz(a, b);
+      r[4 * h + e] = pk[0];
+      r[4 * h + e + 1] = pk[1];
+    }
+  }
+  return r;
+}
 
 // Partial S^T of key sub-tile kt over this wave's dims: rows = keys 16 kt + 4 g + j, columns
 // = heads.  K fragments are read as e4m3 (8 bytes per lane, all eight issued first) and
 // decoded exactly to fp16 in registers; the two latent blocks are accumulated apart and
 // scaled by their key's scale; the RoPE part runs on bf16 MFMA with both operands exact.
-template <int ROPE, int DH>
+template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* qr_lane,
-                                        const f16x8 (&qb)[2][8], int kt, f32x4 (&sk)[2],
-                                        int g16, int c16) {
-  constexpr int RS = MlaGeom<ROPE>::RS;
-  const unsigned char* krow = raw + (kt * 16 + c16) * RS + 256 * DH + 8 * g16;
+                                        const typename QFrag<FMT>::type (&qb)[2][8], int kt,
+                                        f32x4 (&sk)[2], int g16, int c16) {
+  using G = MlaGeom<ROPE, FMT>;
+  constexpr int RS = G::RS;
   f32x4 t0[2], t1[2], tr[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
@@ -141,6 +177,40 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
     t1[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     tr[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if constexpr (FMT == kFmtBf16) {
+    // bf16 K fragments (16 bytes per lane) straight into bf16 MFMA; no scales.
+    const unsigned char* krow = raw + (kt * 16 + c16) * RS + 2 * (256 * DH + 8 * g16);
+    bf16x8 kf[8];
+#pragma unroll
+    for (int i = 0; i < kQkAhead; ++i) kf[i] = *reinterpret_cast<const bf16x8*>(krow + 64 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + kQkAhead < 8)
+        kf[i + kQkAhead] = *reinterpret_cast<const bf16x8*>(krow + 64 * (i + kQkAhead));
+      if (i < 4) {
+        t0[0] = mfma_bf16(kf[i], qb[0][i], t0[0]);
+        t0[1] = mfma_bf16(kf[i], qb[1][i], t0[1]);
+      } else {
+        t1[0] = mfma_bf16(kf[i], qb[0][i], t1[0]);
+        t1[1] = mfma_bf16(kf[i], qb[1][i], t1[1]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(
+          raw + (kt * 16 + c16) * RS + G::ROPE_OFF + 2 * (32 * DH + 8 * g16));
+      const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
+      const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
+      tr[0] = mfma_bf16(kr, q0, tr[0]);
+      tr[1] = mfma_bf16(kr, q1, tr[1]);
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) sk[ht] = (t0[ht] + t1[ht]) + tr[ht];
+    return;
+  }
+  if constexpr (FMT == kFmtFp8) {
+  const unsigned char* krow = raw + (kt * 16 + c16) * RS + 256 * DH + 8 * g16;
   u32x2 kw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) kw[i] = *reinterpret_cast<const u32x2*>(krow + 32 * i);
@@ -161,7 +231,7 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
   __builtin_amdgcn_sched_barrier(0);
   if (ROPE) {
     const bf16x8 kr = *reinterpret_cast<const bf16x8*>(
-        raw + (kt * 16 + c16) * RS + kRopeOff + 2 * (32 * DH + 8 * g16));
+        raw + (kt * 16 + c16) * RS + G::ROPE_OFF + 2 * (32 * DH + 8 * g16));
     const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
     const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
     tr[0] = mfma_bf16(kr, q0, tr[0]);
@@ -177,6 +247,7 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sk[ht][j] = fmaf(t1[ht][j], sc[j][1], fmaf(t0[ht][j], sc[j][0], tr[ht][j]));
+  }
 }
 
 // O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.  V^T fragments
@@ -184,11 +255,39 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
 // (2e, 2e+1) addresses row kp(g, e) = 16 (e >> 2) + 4 g + (e & 3) (bytes 8 (lane & 1) of the
 // fragment's 16 dims), and lane (g, i) receives dim i of rows kp(g, 0..7) -- the key order of
 // the P^T operand taken from the S^T accumulators in place.
-template <int ROPE, int DH>
+template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&pv)[2][2][4],
                                         f32x4 (&o_acc)[2][16], bool& sc_bad, int g16,
                                         int c16) {
-  constexpr int RS = MlaGeom<ROPE>::RS;
+  constexpr int RS = MlaGeom<ROPE, FMT>::RS;
+  if constexpr (FMT == kFmtBf16) {
+    // V^T from the bf16 rows by ds_read_b64_tr_b16: lane (g, i) supplies keys {4g + i/4}
+    // (then 16 + ...) x dims {16 dt + 4 (i%4) .. +3}, receives dim 16 dt + i of keys
+    // 4g .. 4g+3 (lo) and 16 + 4g .. (hi); decoded to fp16 for the fp16 MFMA.
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const unsigned char* vbase =
+        raw + (4 * g16 + (c16 >> 2)) * RS + 2 * (256 * DH + 4 * (c16 & 3));
+    f16x8 pb[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)pv[ht][e >> 2][e & 3];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned char* src = vbase + 32 * dt;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(const_cast<unsigned char*>(src)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(const_cast<unsigned char*>(src + 16 * RS)));
+      const f16x8 va = bf16x8_to_f16(lo, hi);
+      o_acc[0][dt] = mfma_f16(va, pb[0], o_acc[0][dt]);
+      o_acc[1][dt] = mfma_f16(va, pb[1], o_acc[1][dt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    (void)sc_bad;
+    return;
+  } else {
   const int e2 = c16 >> 1;
   const int kp = 16 * (e2 >> 2) + 4 * g16 + (e2 & 3);
   const unsigned char* vbase = raw + kp * RS + 256 * DH + 8 * (c16 & 1);
@@ -228,12 +327,13 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  }
 }
 
-template <int ROPE>
+template <int ROPE, int FMT>
 __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit,
                                                          int keys_per_split, float* part) {
-  using G = MlaGeom<ROPE>;
+  using G = MlaGeom<ROPE, FMT>;
   constexpr int NT = kMlaThreads;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   f32x4* xs = reinterpret_cast<f32x4*>(smem + G::OFF_XS);
@@ -259,7 +359,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     if (tid == 0 && blockIdx.y == 0 && split == 0) raise_fault(a.fault, kFaultQpos);
     row_ok = false;
   }
-  int nsel = a.len[r];
+  // Selected keys: the row's top-k list, or in window mode the last `window` positions.
+  int nsel = a.window > 0 ? min(a.window, p + 1) : a.len[r];
   if (nsel < 0 || nsel > a.top_k) {
     if (tid == 0 && blockIdx.y == 0 && split == 0) raise_fault(a.fault, kFaultTopk);
     nsel = max(0, min(nsel, a.top_k));
@@ -271,12 +372,12 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int ntiles = (nkeys + kTK - 1) / kTK;
 
   // Physical slot of every selected key of this split (-1: outside [0, p] or bad block).
-  const int32_t* sel = a.idx + (size_t)r * a.top_k;
+  const int32_t* sel = a.window > 0 ? nullptr : a.idx + (size_t)r * a.top_k;
   const int32_t* bt = s.block_table + (size_t)b * s.mbps;
   for (int i = tid; i < ntiles * kTK; i += NT) {
     int slot = -1;
     if (i < nkeys) {
-      const int t = sel[k_begin + i];
+      const int t = a.window > 0 ? p - nsel + 1 + k_begin + i : sel[k_begin + i];
       if (t < 0 || t > p) {
         raise_fault(a.fault, kFaultTopk);
       } else {
@@ -310,7 +411,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const uint8_t* zero_row = g_zero_row;
   asm volatile("" : "+s"(zero_row));   // loaded once, not re-fetched from the GOT per tile
   auto issue = [&](int tile, int lane) {
-    const uint32_t stage = lds0 + (uint32_t)((tile % kNStage) * G::STAGE);
+    const uint32_t stage = lds0 + (uint32_t)((tile % G::NSTAGE) * G::STAGE);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     int slot[G::PER_WAVE], off[G::PER_WAVE];
 #pragma unroll
@@ -324,7 +425,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
     for (int u = 0; u < G::PER_WAVE; ++u) {
       const int m = wv + u * kMlaWaves;
-      const uint8_t* src = slot[u] >= 0 ? pool + (int64_t)slot[u] * kLatRow + off[u] : zero_row;
+      const uint8_t* src =
+          slot[u] >= 0 ? pool + (int64_t)slot[u] * G::ROW_BYTES + off[u] : zero_row;
       const uint32_t dst = m < G::NBLK ? stage + (uint32_t)(m * 1024) : lds0 + G::OFF_JUNK;
       dma16(src, dst);
     }
@@ -334,7 +436,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int g16 = lane0 >> 4, c16 = lane0 & 15;
   const bool ht_live[2] = {h0 < H, h0 + 16 < H};
   const bool active = ht_live[0];
-  f16x8 qb[2][8];
+  typename QFrag<FMT>::type qb[2][8];
   bool q_range = true;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
@@ -344,11 +446,15 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * i);
+      if constexpr (FMT == kFmtBf16) {
+        qb[ht][i] = v;                   // bf16 rows: bf16 MFMA, the query as given
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)v[e];
-        q_range &= fabsf(f) <= kF16Max;
-        qb[ht][i][e] = (_Float16)f;      // exact for bf16 values inside the fp16 range
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)v[e];
+          q_range &= fabsf(f) <= kF16Max;
+          qb[ht][i][e] = (_Float16)f;    // exact for bf16 values inside the fp16 range
+        }
       }
     }
   }
@@ -365,7 +471,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   bool sc_bad = false;   // a latent scale that could push P * scale out of fp16
 
 #pragma unroll
-  for (int t = 0; t < kNStage - 1; ++t)
+  for (int t = 0; t < G::NSTAGE - 1; ++t)
     if (t < ntiles) issue(t, lane0);
   for (int tile = 0; tile < ntiles; ++tile) {
     // Lane-derived addresses are recomputed every tile (a few VALU instructions) rather than
@@ -373,14 +479,14 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     int lane = lane0;
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, c16 = lane & 15;
-    const unsigned char* raw = smem + (tile % kNStage) * G::STAGE;
+    const unsigned char* raw = smem + (tile % G::NSTAGE) * G::STAGE;
     // This tile's transfers are the oldest outstanding ones: later tiles may stay in flight.
-    const int ahead = min(kNStage - 2, ntiles - 1 - tile);
+    const int ahead = min(G::NSTAGE - 2, ntiles - 1 - tile);
     if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
     else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
     else wait_vmcnt<0>();
     __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
-    if (tile + kNStage - 1 < ntiles) issue(tile + kNStage - 1, lane);
+    if (tile + G::NSTAGE - 1 < ntiles) issue(tile + G::NSTAGE - 1, lane);
 
     // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
     //      partner waves then add half 0 + half 1 in the same order
@@ -390,8 +496,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 sk[2];
-        if (dh == 0) qk_part<ROPE, 0>(raw, qr_lane, qb, kt, sk, g16, c16);
-        else qk_part<ROPE, 1>(raw, qr_lane, qb, kt, sk, g16, c16);
+        if (dh == 0) qk_part<ROPE, FMT, 0>(raw, qr_lane, qb, kt, sk, g16, c16);
+        else qk_part<ROPE, FMT, 1>(raw, qr_lane, qb, kt, sk, g16, c16);
         mine[(2 * kt) * kWave + lane] = sk[0];
         mine[(2 * kt + 1) * kWave + lane] = sk[1];
       }
@@ -448,8 +554,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T over this wave's dim half
-    if (dh == 0) pv_part<ROPE, 0>(raw, pv, o_acc, sc_bad, g16, c16);
-    else pv_part<ROPE, 1>(raw, pv, o_acc, sc_bad, g16, c16);
+    if (dh == 0) pv_part<ROPE, FMT, 0>(raw, pv, o_acc, sc_bad, g16, c16);
+    else pv_part<ROPE, FMT, 1>(raw, pv, o_acc, sc_bad, g16, c16);
   }
 
   if (__any(sc_bad) && lane0 == 0) raise_fault(a.fault, kFaultRange);
@@ -489,9 +595,9 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   (void)c16;
 }
 
-template <int ROPE>
+template <int ROPE, int FMT>
 constexpr size_t mla_lds_bytes() {
-  return (size_t)MlaGeom<ROPE>::BYTES;
+  return (size_t)MlaGeom<ROPE, FMT>::BYTES;
 }
 
 // Merge split partials: o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) (base-2 lse).
@@ -626,18 +732,18 @@ MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
   return pl;
 }
 
-template <int ROPE>
-hipError_t launch_fp8(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
-  constexpr size_t lds = mla_lds_bytes<ROPE>();
+template <int ROPE, int FMT>
+hipError_t launch_rows(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
+  constexpr size_t lds = mla_lds_bytes<ROPE, FMT>();
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8<ROPE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8<ROPE, FMT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   dim3 grid(a.s.total_q, pl.groups, pl.nsplit);
-  k_mla_fp8<ROPE><<<grid, kMlaThreads, lds, st>>>(a, pl.nsplit, pl.keys_per_split, part);
+  k_mla_fp8<ROPE, FMT><<<grid, kMlaThreads, lds, st>>>(a, pl.nsplit, pl.keys_per_split, part);
   return hipGetLastError();
 }
 
@@ -656,7 +762,13 @@ hipError_t launch_mla(const MlaLaunch& a, hipStream_t st) {
   }
   const MlaPlan pl = plan_mla(a.s, a.n_heads, a.top_k);
   float* part = pl.nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
-  hipError_t e = a.rope_dim ? launch_fp8<64>(a, pl, part, st) : launch_fp8<0>(a, pl, part, st);
+  hipError_t e;
+  if (a.bf16_rows)
+    e = a.rope_dim ? launch_rows<64, kFmtBf16>(a, pl, part, st)
+                   : launch_rows<0, kFmtBf16>(a, pl, part, st);
+  else
+    e = a.rope_dim ? launch_rows<64, kFmtFp8>(a, pl, part, st)
+                   : launch_rows<0, kFmtFp8>(a, pl, part, st);
   if (e != hipSuccess || pl.nsplit <= 1) return e;
   k_mla_combine<<<dim3(a.s.total_q, a.n_heads), 128, 0, st>>>(a, pl.nsplit, part);
   return hipGetLastError();

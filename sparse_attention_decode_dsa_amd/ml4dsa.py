@@ -21,13 +21,13 @@ ML4_OK, ML4_E_INVALID, ML4_E_UNSUPPORTED, ML4_E_WORKSPACE, ML4_E_LAUNCH, ML4_E_D
     0, -1, -2, -3, -4, -5)
 ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
 ML4_IDX_F32, ML4_IDX_FP8_132 = 0, 1
-ML4_LAT_F32, ML4_LAT_FP8_656 = 0, 1
+ML4_LAT_F32, ML4_LAT_FP8_656, ML4_LAT_BF16_1152 = 0, 1, 2
 ML4_FAULT_BLOCK_ID, ML4_FAULT_TOPK_INDEX, ML4_FAULT_NAN_SCORE, ML4_FAULT_QPOS = 1, 2, 4, 8
 ML4_FAULT_RANGE = 16
 ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
-           "ml4_sparse_attn_layer", "ml4_index_cache_write", "ml4_latent_cache_write",
+           "ml4_sparse_attn_layer", "ml4_window_mla_decode", "ml4_index_cache_write", "ml4_latent_cache_write",
            "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
            "ml4_fault_query", "ml4_abi_version")
 
@@ -93,6 +93,9 @@ def _load() -> C.CDLL:
     lib.ml4_latent_cache_write.restype = C.c_int
     lib.ml4_latent_cache_write.argtypes = [P(ml4_cache), i32, vp, i32, vp, i32, i64, vp, vp,
                                            vp]
+    lib.ml4_window_mla_decode.restype = C.c_int
+    lib.ml4_window_mla_decode.argtypes = [P(ml4_seqs), P(ml4_cache), vp, i32, i32, i32, i32,
+                                          f32, f32, vp, i32, vp, vp, sz, vp, vp]
     lib.ml4_topk_merge.restype = C.c_int
     lib.ml4_topk_merge.argtypes = [i32, i32, vp, vp, vp, i64, i32, vp, vp, vp, vp]
     lib.ml4_lse_combine.restype = C.c_int
@@ -246,4 +249,14 @@ def ml4_lse_combine(rows, n_heads, n_shards, head_dim, o_parts, lse_parts, out, 
                     lse=None, stream=None, check=True) -> int:
     rc = LIB.ml4_lse_combine(rows, n_heads, n_shards, head_dim, ptr(o_parts), ptr(lse_parts),
                              ptr(out), out_dtype, ptr(lse), stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_window_mla_decode(seqs, kv, q, q_dtype, n_heads, rope_dim, window, softmax_scale,
+                          ssmax_s, out, out_dtype, lse=None, ws=None, ws_bytes=0, fault=None,
+                          stream=None, check=True) -> int:
+    rc = LIB.ml4_window_mla_decode(C.byref(seqs), C.byref(kv), ptr(q), q_dtype, n_heads,
+                                   rope_dim, window, softmax_scale, ssmax_s, ptr(out),
+                                   out_dtype, ptr(lse), ptr(ws), ws_bytes, ptr(fault),
+                                   stream_handle(stream))
     return _check(rc) if check else rc
