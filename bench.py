@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cache-write-tokens", type=int, default=65536,
                     help="also time the KV-cache write entries on this many bf16 tokens "
                          "(0 = skip); reported beside the step, not in it")
+    ap.add_argument("--no-layouts", action="store_true",
+                    help="skip the side measurements of the bf16-row layout and of "
+                         "sliding-window attention")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused entry instead (no per-kernel events)")
     return ap.parse_args()
@@ -157,6 +160,60 @@ def cpu_baseline(case, budget_s: float):
             "kind": "oracle",
             "sample": f"{rows_done} query rows ({len(sample)} whole requests), every layer of "
                       f"the step, fp64 numpy oracle; {elapsed:.1f} s of compute"}
+
+
+def time_layouts(case, run, dev: str, reps: int = 10):
+    """Side measurements on the workload's first layer, outside the step: the same sparse
+    MLA over a bf16 1,152-byte-row copy of the latent cache (same selections), and
+    sliding-window MLA (2,048 positions) over the fp8 cache.  Work per launch as for the
+    step's MLA: FLOPs 2 H (1024 + rope) per (row, key), bytes per selected row."""
+    import torch
+
+    from sparse_attention_decode_dsa_amd import ml4dsa as M
+    from sparse_attention_decode_dsa_amd import synth
+    d = case.layers[0]
+    l = d["layer"]
+    b = case.batch
+    H, rope, K = case.mla_heads, d["rope_dim"], d["top_k"]
+    li = case.inputs[l]
+    nb, bs = li.lat_pool.shape[0], li.lat_pool.shape[1]
+    pool16 = synth.make_latent_pool(77, nb, bs, "bf16", device=dev)
+    c16 = M.make_cache(pool16, M.ML4_LAT_BF16_1152)
+    idx, ln = run.topk_of(l)
+    out = torch.empty((b.total_q, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b.total_q, H), dtype=torch.float32, device=dev)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_MLA, run.seqs, H, K)
+    ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=dev)
+    fault = torch.zeros(1, dtype=torch.int32, device=dev)
+    qpos = b.q_pos.cpu()
+    nsel = int(ln.clamp(min=0).sum().item())
+    nwin = int(torch.clamp(qpos + 1, max=K).sum().item())
+    res = {}
+    for name, fn, nkeys, row_b in (
+            ("bf16_rows_sparse", lambda: M.ml4_sparse_mla_decode(
+                run.seqs, c16, li.q_mla, M.ML4_BF16, H, rope, idx, ln, K, d["softmax_scale"],
+                d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault), nsel,
+             1152 if rope else 1024),
+            ("window2048_fp8", lambda: M.ml4_window_mla_decode(
+                run.seqs, run.lat_caches[l], li.q_mla, M.ML4_BF16, H, rope, K,
+                d["softmax_scale"], d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault), nwin,
+             656 if rope else 528)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        flops = 2.0 * H * (1024 + rope) * nkeys
+        res[name] = {"us": us, "TFLOPs": flops / (us * 1e-6) / 1e12,
+                     "frac_f16_peak": flops / (us * 1e-6) / 1e12 / PEAK_F16_TFLOPS,
+                     "row_bytes": row_b, "GBps_rows": nkeys * row_b / (us * 1e-6) / 1e9}
+    assert M.ml4_fault_query(fault) == 0
+    del pool16
+    return res
 
 
 def time_cache_writes(n: int, dev: str, reps: int = 10):
@@ -316,6 +373,8 @@ def main():
         roof["avg_launch_us"] = us
         roof["traffic"] = load_traffic(dom)
         result["roofline"] = roof
+    if not args.no_layouts and case.fmt == "fp8":
+        result["layouts"] = time_layouts(case, run, dev)
     if args.cache_write_tokens > 0:
         result["cache_write"] = time_cache_writes(args.cache_write_tokens, dev)
     if args.cpu_seconds > 0:
