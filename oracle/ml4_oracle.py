@@ -58,6 +58,13 @@ Page titles used below:
        LSE:    M = max_s lse_s,  o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M),
                lse = M + ln sum_s e^(lse_s - M)  (shards with lse = -inf contribute nothing).
 
+8. Second latent layouts  [blog, ROCm implementation details › "FP8 潜在缓存" (the ROCm path
+   stores the latent as plain E4M3, 576 B per token with one per-tensor scale, and quantises
+   the queries to FP8; the uncompressed row is 576 bf16 values, 1,152 B)]: the plain E4M3
+   row is [512 E4M3 latent][64 E4M3 RoPE], value = code * kv_scale; an FP8 query is E4M3
+   codes with one fp32 scale per (row, head), value = code * q_scale.  The attention
+   formula is step 3's on those values.
+
 Every step is the plain definition, in fp64, in the pages' order; numpy matrix products
 serve as the only library primitive.
 """
@@ -205,6 +212,16 @@ def latent_rows_bf16(pool: np.ndarray, s: np.ndarray, rope_dim: int
     return decode_bf16(flat[:, :KV_LORA]), decode_bf16(flat[:, KV_LORA:KV_LORA + rope_dim])
 
 
+def latent_rows_e4m3(pool: np.ndarray, s: np.ndarray, rope_dim: int, kv_scale: float
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """pool: uint8 [num_blocks, block_size, 576] plain E4M3 rows (512 latent then 64 RoPE),
+    one per-tensor scale.  With rope_dim == 0 the RoPE codes are never read."""
+    flat = pool.reshape(-1, KV_LORA + ROPE_DIM)[s]
+    c = decode_e4m3(flat[:, :KV_LORA]) * float(kv_scale)
+    kr = decode_e4m3(flat[:, KV_LORA:KV_LORA + rope_dim]) * float(kv_scale)
+    return c, kr
+
+
 def window_positions(q_pos: np.ndarray, window: int) -> Tuple[np.ndarray, np.ndarray]:
     """Sliding-window selection [blog, Long context (DSpark draft layers: a 2,048-token
     window)]: row r attends to max(0, p_r - window + 1) .. p_r.  Returned in the top-k list
@@ -288,12 +305,15 @@ def topk_select(scores: np.ndarray, q_pos: np.ndarray, top_k: int
 # --------------------------------------------------------------------------------------
 def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: int,
                topk_idx: np.ndarray, topk_len: np.ndarray, softmax_scale: float,
-               ssmax_s: float, rows: Optional[Sequence[int]] = None
+               ssmax_s: float, rows: Optional[Sequence[int]] = None,
+               q_scale: Optional[np.ndarray] = None, kv_scale: float = 1.0
                ) -> Tuple[np.ndarray, np.ndarray]:
     """o [len(rows), H, 512] and lse [len(rows), H] in fp64.
 
     fmt 'fp8': pool uint8 [nb, bs, 656]; q uint16 bf16 bits [total_q, H, 512 + rope_dim].
     fmt 'bf16': pool uint16 bf16 bits [nb, bs, 576]; q as for 'fp8'.
+    fmt 'e4m3': pool uint8 [nb, bs, 576] plain E4M3 rows times kv_scale; q uint8 E4M3 codes
+                [total_q, H, 512 + rope_dim] times q_scale [total_q, H].
     fmt 'f32': pool float32 [nb, bs, 576]; q float32 [total_q, H, 512 + rope_dim].
     topk_idx holds logical positions; entries past topk_len[r] are ignored.
     """
@@ -314,6 +334,9 @@ def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: 
         elif fmt == "bf16":
             c, kr = latent_rows_bf16(pool, s, rope_dim)
             qv = decode_bf16(q[r])
+        elif fmt == "e4m3":
+            c, kr = latent_rows_e4m3(pool, s, rope_dim, kv_scale)
+            qv = decode_e4m3(q[r]) * np.asarray(q_scale[r], dtype=np.float64)[:, None]
         else:
             c, kr = latent_rows_f32(pool, s, rope_dim)
             qv = np.asarray(q[r], dtype=np.float64)

@@ -173,6 +173,31 @@ def make_latent_pool(seed: int, num_blocks: int, block_size: int, fmt: str,
     return out.view(num_blocks, block_size, row)
 
 
+def make_plain_e4m3_pool(seed: int, num_blocks: int, block_size: int, device="cpu",
+                         chunk_tokens: int = 1 << 19):
+    """Plain E4M3 latent rows (576 codes: 512 latent then 64 RoPE) with one per-tensor
+    scale: N(0,1) values quantised with scale 4.5 / 448 (values beyond 4.5 saturate).
+    Returns (pool uint8 [num_blocks, block_size, 576], scale)."""
+    g = _gen(seed, device)
+    ntok = num_blocks * block_size
+    scale = 4.5 / E4M3_MAX
+    out = torch.empty((ntok, KV_LORA + ROPE_DIM), dtype=torch.uint8, device=device)
+    for s in range(0, ntok, chunk_tokens):
+        e = min(ntok, s + chunk_tokens)
+        x = torch.randn((e - s, KV_LORA + ROPE_DIM), generator=g, device=device)
+        out[s:e] = _to_e4m3_codes(x, torch.tensor(scale, device=device))
+    return out.view(num_blocks, block_size, KV_LORA + ROPE_DIM), scale
+
+
+def make_mla_query_fp8(seed: int, total_q: int, heads: int, rope_dim: int, device="cpu"):
+    """FP8 MLA queries: E4M3 codes [total_q, heads, 512 + rope_dim] with one amax/448
+    scale per (row, head)."""
+    g = _gen(seed, device)
+    q = torch.randn((total_q, heads, KV_LORA + rope_dim), generator=g, device=device)
+    sc = _amax_scale(q)
+    return _to_e4m3_codes(q, sc), sc.squeeze(-1).contiguous()
+
+
 def make_index_query(seed: int, total_q: int, heads: int, fmt: str, device="cpu"):
     g = _gen(seed, device)
     q = torch.randn((total_q, heads, IDX_DIM), generator=g, device=device)

@@ -538,3 +538,33 @@ def test_bf16_rows_and_window_selection_reduce_to_dense_attention():
     o, lse = O.sparse_mla(seqs, bits, "bf16", q, 64, widx, wln, 0.05, 0.0)
     od, lsed = O.dense_mla(seqs, bits, "bf16", q, 64, 0.05, 0.0)
     assert np.allclose(o, od, atol=1e-12) and np.allclose(lse, lsed)
+
+
+def test_plain_e4m3_rows_equal_fp8_ds_mla_rows_with_uniform_power_of_two_scales():
+    """A plain E4M3 576-B row with per-tensor scale 2^-5 and an FP8 query with scales 2^-3
+    are the same values as an fp8_ds_mla row whose four group scales are 2^-5 and whose
+    bf16 RoPE holds the decoded RoPE codes times 2^-5, with a bf16 query of the decoded
+    codes times 2^-3 (all exact): attention over both is identical."""
+    g = np.random.default_rng(10)
+    n, H = 40, 4
+    codes = g.integers(0, 256, (n, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00                    # no NaN codes
+    ks = 2.0 ** -5
+    plain = codes.reshape(1, n, 576)
+    ds = np.zeros((1, n, 656), dtype=np.uint8)
+    ds[0, :, :512] = codes[:, :512]
+    ds[0, :, 512:528] = np.frombuffer(np.full(4 * n, ks, dtype="<f4").tobytes(),
+                                      dtype=np.uint8).reshape(n, 16)
+    rope_vals = O.decode_e4m3(codes[:, 512:]) * ks
+    ds[0, :, 528:] = P.bf16_bits(rope_vals.astype(np.float32)).view(np.uint8).reshape(n, 128)
+    qc = g.integers(0, 256, (2, H, 576)).astype(np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x38
+    qs = np.full((2, H), 2.0 ** -3)
+    qbf = P.bf16_bits((O.decode_e4m3(qc) * 2.0 ** -3).astype(np.float32))
+    seqs = O.Seqs(np.array([n]), np.array([0, 2]), np.array([30, 39]), np.arange(1)[None, :], n)
+    idx, ln = O.window_positions(seqs.q_pos, 64)
+    for rope in (64, 0):
+        a = O.sparse_mla(seqs, plain, "e4m3", qc[..., :512 + rope], rope, idx, ln, 0.05, 0.3,
+                         q_scale=qs, kv_scale=ks)
+        b = O.sparse_mla(seqs, ds, "fp8", qbf[..., :512 + rope], rope, idx, ln, 0.05, 0.3)
+        assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
