@@ -164,9 +164,10 @@ def cpu_baseline(case, budget_s: float):
 
 def time_layouts(case, run, dev: str, reps: int = 10):
     """Side measurements on the workload's first layer, outside the step: the same sparse
-    MLA over a bf16 1,152-byte-row copy of the latent cache (same selections), and
-    sliding-window MLA (2,048 positions) over the fp8 cache.  Work per launch as for the
-    step's MLA: FLOPs 2 H (1024 + rope) per (row, key), bytes per selected row."""
+    MLA over a bf16 1,152-byte-row copy of the latent cache and over a plain-E4M3 576-byte-row
+    copy with FP8 queries (same selections), and sliding-window MLA (2,048 positions) over
+    the fp8 cache.  Work per launch as for the step's MLA: FLOPs 2 H (1024 + rope) per
+    (row, key), bytes per selected row."""
     import torch
 
     from sparse_attention_decode_dsa_amd import ml4dsa as M
@@ -179,6 +180,9 @@ def time_layouts(case, run, dev: str, reps: int = 10):
     nb, bs = li.lat_pool.shape[0], li.lat_pool.shape[1]
     pool16 = synth.make_latent_pool(77, nb, bs, "bf16", device=dev)
     c16 = M.make_cache(pool16, M.ML4_LAT_BF16_1152)
+    pool8, kv_scale = synth.make_plain_e4m3_pool(78, nb, bs, device=dev)
+    c8 = M.make_cache(pool8, M.ML4_LAT_E4M3_576)
+    q8, q8s = synth.make_mla_query_fp8(79, b.total_q, H, rope, device=dev)
     idx, ln = run.topk_of(l)
     out = torch.empty((b.total_q, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b.total_q, H), dtype=torch.float32, device=dev)
@@ -194,6 +198,10 @@ def time_layouts(case, run, dev: str, reps: int = 10):
                 run.seqs, c16, li.q_mla, M.ML4_BF16, H, rope, idx, ln, K, d["softmax_scale"],
                 d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault), nsel,
              1152 if rope else 1024),
+            ("e4m3_rows_sparse", lambda: M.ml4_sparse_mla_decode_e4m3(
+                run.seqs, c8, kv_scale, q8, q8s, H, rope, idx, ln, K, d["softmax_scale"],
+                d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault), nsel,
+             576 if rope else 528),
             ("window2048_fp8", lambda: M.ml4_window_mla_decode(
                 run.seqs, run.lat_caches[l], li.q_mla, M.ML4_BF16, H, rope, K,
                 d["softmax_scale"], d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault), nwin,
@@ -212,7 +220,7 @@ def time_layouts(case, run, dev: str, reps: int = 10):
                      "frac_f16_peak": flops / (us * 1e-6) / 1e12 / PEAK_F16_TFLOPS,
                      "row_bytes": row_b, "GBps_rows": nkeys * row_b / (us * 1e-6) / 1e9}
     assert M.ml4_fault_query(fault) == 0
-    del pool16
+    del pool16, pool8, q8, q8s
     return res
 
 

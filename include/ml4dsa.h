@@ -36,7 +36,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 
-#define ML4_ABI_VERSION 2
+#define ML4_ABI_VERSION 3
 
 enum ml4_status {
   ML4_OK = 0,
@@ -62,8 +62,10 @@ enum ml4_index_format {
 enum ml4_latent_format {
   ML4_LAT_F32 = 0,      /* [512 x fp32 latent][64 x fp32 RoPE] = 2,304 B (fp32 test format) */
   ML4_LAT_FP8_656 = 1,  /* [512 x e4m3][4 x fp32 scale, one per 128][64 x bf16 RoPE] = 656 B */
-  ML4_LAT_BF16_1152 = 2 /* [512 x bf16][64 x bf16 RoPE] = 1,152 B ([blog] FP8 潜在缓存: the
+  ML4_LAT_BF16_1152 = 2, /* [512 x bf16][64 x bf16 RoPE] = 1,152 B ([blog] FP8 潜在缓存: the
                            uncompressed bf16 row the FP8 layouts are measured against)     */
+  ML4_LAT_E4M3_576 = 3  /* [512 x e4m3][64 x e4m3 RoPE] = 576 B, value = code * kv_scale with
+                           one per-tensor scale ([blog] FP8 潜在缓存: the ROCm layout)       */
 };
 
 #define ML4_IDX_DIM 128
@@ -176,6 +178,30 @@ int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
                           float softmax_scale, float ssmax_s, void* out, int32_t out_dtype,
                           float* lse, void* ws, size_t ws_bytes, uint32_t* fault,
                           hipStream_t stream);
+
+/*
+ * ml4_sparse_mla_decode_e4m3 -- ml4_sparse_mla_decode over plain E4M3 latent rows with FP8
+ * queries.  [blog, ROCm implementation details › FP8 潜在缓存 (all 576 latent dims stored as
+ * E4M3 with one per-tensor scale, 576 B per token per layer; the queries are quantised to FP8
+ * as well, so QK runs FP8 x FP8)]
+ *   The formula of ml4_sparse_mla_decode on the decoded values
+ *     c_t|kr_t = e4m3(code) * kv_scale,   qa|qr[r][h] = e4m3(q code) * q_scale[r][h].
+ *   kv       an ML4_LAT_E4M3_576 cache.   kv_scale: finite, > 0.
+ *   q        [total_q][n_heads][512 + rope_dim] e4m3 codes (OCP E4M3FN), 16-B aligned.
+ *   q_scale  [total_q][n_heads] fp32 (a non-finite scale raises ML4_FAULT_RANGE).
+ *   out      [total_q][n_heads][512] bf16 (out_dtype ML4_BF16).   lse: fp32 or NULL.
+ *   Other arguments, workspace and fault bits as for ml4_sparse_mla_decode.
+ * QK runs on FP8 MFMA with fp32 accumulation (products exact; the hardware's 128-term sum may
+ * drop low-order bits of small products); PV decodes V exactly to fp16 and runs on fp16 MFMA
+ * with the softmax weights rounded to fp16; kv_scale multiplies the normalised output.
+ */
+int ml4_sparse_mla_decode_e4m3(const ml4_seqs* s, const ml4_cache* kv, float kv_scale,
+                               const uint8_t* q, const float* q_scale, int32_t n_heads,
+                               int32_t rope_dim, const int32_t* topk_idx,
+                               const int32_t* topk_len, int32_t top_k, float softmax_scale,
+                               float ssmax_s, void* out, int32_t out_dtype, float* lse,
+                               void* ws, size_t ws_bytes, uint32_t* fault,
+                               hipStream_t stream);
 
 /*
  * ml4_window_mla_decode -- MLA over the last `window` positions of each row (a sliding

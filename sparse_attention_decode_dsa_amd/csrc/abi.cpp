@@ -93,7 +93,7 @@ void check_cache(Checks& c, const ml4_cache* k, bool index, const char* name) {
   if (index && k->format != ML4_IDX_F32 && k->format != ML4_IDX_FP8_132)
     c.invalid.push_back(n + ".format is not an ml4_index_format");
   if (!index && k->format != ML4_LAT_F32 && k->format != ML4_LAT_FP8_656 &&
-      k->format != ML4_LAT_BF16_1152)
+      k->format != ML4_LAT_BF16_1152 && k->format != ML4_LAT_E4M3_576)
     c.invalid.push_back(n + ".format is not an ml4_latent_format");
 }
 
@@ -160,12 +160,14 @@ void check_mla(Checks& c, const ml4_cache* kv, const void* q, int32_t q_dtype, i
           "an ML4_LAT_FP8_656 / ML4_LAT_BF16_1152 cache writes ML4_BF16 outputs");
     c.bad(kv->format == ML4_LAT_F32 && (q_dtype != ML4_F32 || out_dtype != ML4_F32),
           "an ML4_LAT_F32 cache needs ML4_F32 queries and outputs");
+    c.bad(kv->format == ML4_LAT_E4M3_576 && (q_dtype != ML4_FP8_E4M3 || out_dtype != ML4_BF16),
+          "an ML4_LAT_E4M3_576 cache needs ML4_FP8_E4M3 queries and ML4_BF16 outputs");
   }
   c.unsup(n_heads < 16 || n_heads > 128 || n_heads % 16 != 0,
           "n_heads must be a multiple of 16 in 16 .. 128");
   c.unsup(rope_dim != 0 && rope_dim != ML4_ROPE_DIM, "rope_dim must be 64 or 0 (NoPE)");
   c.bad(window == 0 && (!idx || !len), "topk_idx and topk_len must be non-NULL");
-  c.unsup(window > 0 && kv && kv->format == ML4_LAT_F32,
+  c.unsup(window > 0 && kv && (kv->format == ML4_LAT_F32 || kv->format == ML4_LAT_E4M3_576),
           "window attention needs an ML4_LAT_FP8_656 or ML4_LAT_BF16_1152 cache");
   c.bad(top_k < 1, "top_k must be >= 1");
   c.unsup(top_k > ML4_MAX_TOPK, "top_k above 2048");
@@ -257,6 +259,8 @@ int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   check_seqs(c, s);
   check_mla(c, kv, q, q_dtype, n_heads, rope_dim, topk_idx, topk_len, top_k, softmax_scale,
             ssmax_s, out, out_dtype);
+  c.bad(kv && kv->format == ML4_LAT_E4M3_576,
+        "an ML4_LAT_E4M3_576 cache carries scales: use ml4_sparse_mla_decode_e4m3");
   if (c.invalid.empty() && c.unsupported.empty()) {
     const size_t need = ml4_workspace_bytes(ML4_ENTRY_MLA, s, n_heads, top_k);
     c.ws(ws_bytes < need, bytes_msg("sparse-MLA workspace", need, ws_bytes));
@@ -282,6 +286,50 @@ int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   a.ws = ws;
   a.fault = fault;
   return launch_status(ml4::launch_mla(a, stream), "ml4_sparse_mla_decode");
+}
+
+int ml4_sparse_mla_decode_e4m3(const ml4_seqs* s, const ml4_cache* kv, float kv_scale,
+                               const uint8_t* q, const float* q_scale, int32_t n_heads,
+                               int32_t rope_dim, const int32_t* topk_idx,
+                               const int32_t* topk_len, int32_t top_k, float softmax_scale,
+                               float ssmax_s, void* out, int32_t out_dtype, float* lse,
+                               void* ws, size_t ws_bytes, uint32_t* fault,
+                               hipStream_t stream) {
+  Checks c;
+  check_seqs(c, s);
+  check_mla(c, kv, q, ML4_FP8_E4M3, n_heads, rope_dim, topk_idx, topk_len, top_k,
+            softmax_scale, ssmax_s, out, out_dtype);
+  c.bad(kv && kv->format != ML4_LAT_E4M3_576, "kv.format must be ML4_LAT_E4M3_576");
+  c.bad(!(kv_scale > 0.f) || !std::isfinite(kv_scale), "kv_scale must be finite and > 0");
+  c.bad(!q_scale, "q_scale is NULL");
+  c.bad(!aligned(q_scale, 4), "q_scale must be 4-byte aligned");
+  if (c.invalid.empty() && c.unsupported.empty()) {
+    const size_t need = ml4_workspace_bytes(ML4_ENTRY_MLA, s, n_heads, top_k);
+    c.ws(ws_bytes < need, bytes_msg("sparse-MLA workspace", need, ws_bytes));
+    c.ws(need && (!ws || !aligned(ws, 256)), "workspace must be non-NULL and 256-byte aligned");
+  }
+  if (int rc = c.finish("ml4_sparse_mla_decode_e4m3")) return rc;
+  ml4::MlaLaunch a{};
+  a.s = view(s);
+  a.pool = kv->pool;
+  a.num_blocks = kv->num_blocks;
+  a.fp8 = true;
+  a.e4m3_rows = true;
+  a.q_scale = q_scale;
+  a.kv_scale = kv_scale;
+  a.q = q;
+  a.n_heads = n_heads;
+  a.rope_dim = rope_dim;
+  a.idx = topk_idx;
+  a.len = topk_len;
+  a.top_k = top_k;
+  a.softmax_scale = softmax_scale;
+  a.ssmax_s = ssmax_s;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.fault = fault;
+  return launch_status(ml4::launch_mla(a, stream), "ml4_sparse_mla_decode_e4m3");
 }
 
 int ml4_window_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
@@ -358,6 +406,9 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
   check_mla(c, &lat_caches[lat_layer], q_mla, q_mla_dtype, L->mla_heads, L->rope_dim,
             topk_bufs[topk_layer], topk_lens[topk_layer], L->top_k, L->softmax_scale, L->ssmax_s,
             out, out_dtype);
+  c.unsup(lat_caches[lat_layer].format == ML4_LAT_E4M3_576,
+          "the fused layer takes ML4_LAT_FP8_656, ML4_LAT_BF16_1152 or ML4_LAT_F32 latent "
+          "caches (ML4_LAT_E4M3_576: ml4_sparse_mla_decode_e4m3)");
   size_t need = 0;
   if (c.invalid.empty() && c.unsupported.empty() && s) {
     need = ml4_workspace_bytes(ML4_ENTRY_LAYER, s, L->mla_heads, L->top_k);

@@ -53,6 +53,9 @@ struct MlaLaunch {
   int64_t num_blocks;
   bool fp8;             // ML4_LAT_FP8_656 / ML4_LAT_BF16_1152 + bf16 q/out; else ML4_LAT_F32
   bool bf16_rows;       // ML4_LAT_BF16_1152
+  bool e4m3_rows;       // ML4_LAT_E4M3_576 with E4M3 queries
+  const float* q_scale; // [total_q][n_heads] (E4M3 queries)
+  float kv_scale;       // per-tensor scale of the E4M3 rows
   int window;           // > 0: attend to the last `window` positions (idx / len unused)
   const void* q;
   int n_heads;

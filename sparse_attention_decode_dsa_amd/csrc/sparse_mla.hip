@@ -99,14 +99,19 @@ __device__ __forceinline__ float sum_over_lane_groups(float v) {
 // matrix-core operands are read from there directly.
 //   FMT kFmtFp8:  fp8_ds_mla rows, [512 e4m3][4 x fp32 scale][64 x bf16 RoPE] = 656 B;
 //   FMT kFmtBf16: bf16 rows, [512 x bf16][64 x bf16 RoPE] = 1,152 B (four-tile ring does not
-//                 fit; two tiles, one in flight).
-constexpr int kFmtFp8 = 0, kFmtBf16 = 1;
+//                 fit; two tiles, one in flight);
+//   FMT kFmtE4m3: plain E4M3 rows, [512 x e4m3][64 x e4m3 RoPE] = 576 B, one per-tensor scale.
+//                 A NoPE layer gathers 33 chunks (528 B) per row: the padding chunk (RoPE
+//                 bytes, never read) keeps rows off a 512-B LDS stride.
+constexpr int kFmtFp8 = 0, kFmtBf16 = 1, kFmtE4m3 = 2;
 
 template <int ROPE, int FMT>
 struct MlaGeom {
-  static constexpr int ROW_BYTES = FMT == kFmtFp8 ? 656 : 1152;     // cache row stride
-  static constexpr int ROPE_OFF = FMT == kFmtFp8 ? 528 : 1024;
-  static constexpr int NCH = (ROPE ? ROW_BYTES : ROPE_OFF) / 16;   // 16-B chunks read per row
+  static constexpr int ROW_BYTES =                                  // cache row stride
+      FMT == kFmtFp8 ? 656 : FMT == kFmtBf16 ? 1152 : 576;
+  static constexpr int ROPE_OFF = FMT == kFmtFp8 ? 528 : FMT == kFmtBf16 ? 1024 : 512;
+  static constexpr int NCH =                                        // 16-B chunks read per row
+      ROPE ? ROW_BYTES / 16 : FMT == kFmtE4m3 ? 33 : ROPE_OFF / 16;
   static constexpr int NSTAGE = FMT == kFmtFp8 ? kNStage : 2;
   static constexpr int RS = 16 * NCH;                   // bytes per gathered row
   static constexpr int RAW = kTK * NCH;                 // chunks per tile
@@ -116,13 +121,15 @@ struct MlaGeom {
   static constexpr int OFF_JUNK = NSTAGE * STAGE;
   static constexpr int OFF_XS = OFF_JUNK + 1024;                      // [8][4][64] f32x4
   static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] bf16
-  static constexpr int OFF_SLOT = OFF_QR + (ROPE ? kHeadsPerWg * kQRS * 2 : 0);
+  static constexpr int OFF_SLOT = OFF_QR + (ROPE && FMT != kFmtE4m3 ? kHeadsPerWg * kQRS * 2 : 0);
   static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
 };
 static_assert(MlaGeom<64, kFmtFp8>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<64, kFmtBf16>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<0, kFmtFp8>::RS == 528 && MlaGeom<64, kFmtFp8>::RS == 656, "rows");
 static_assert(MlaGeom<0, kFmtBf16>::RS == 1024 && MlaGeom<64, kFmtBf16>::RS == 1152, "rows");
+static_assert(MlaGeom<64, kFmtE4m3>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<0, kFmtE4m3>::RS == 528 && MlaGeom<64, kFmtE4m3>::RS == 576, "rows");
 
 // Work split inside a work-group of 8 waves (one query row, up to 128 heads): wave w owns
 // head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half dh = w >> 2
@@ -135,10 +142,12 @@ constexpr int kQkAhead = 2;   // bf16 K fragments in flight ahead of the MFMAs
 // Scale offset of an fp8_ds_mla row.
 constexpr int kScaleOff = 512;
 
-// Query-fragment register type: fp16 for the e4m3 rows (decoded exactly to fp16), bf16 as
-// given for the bf16 rows.
-template <int FMT> struct QFrag { typedef f16x8 type; };
-template <> struct QFrag<kFmtBf16> { typedef bf16x8 type; };
+// Query fragments per head tile: fp16 for the fp8_ds_mla rows (decoded exactly to fp16),
+// bf16 as given for the bf16 rows (8 x 32 dims each), E4M3 codes for the plain E4M3 rows
+// (two 128-dim latent fragments and one RoPE fragment, 32 bytes per lane each).
+template <int FMT> struct QFrag { typedef f16x8 type; static constexpr int N = 8; };
+template <> struct QFrag<kFmtBf16> { typedef bf16x8 type; static constexpr int N = 8; };
+template <> struct QFrag<kFmtE4m3> { typedef i32x8 type; static constexpr int N = 3; };
 
 // Eight bf16 values (four per 64-bit half) -> fp16, exactly for |x| in [2^-14, 65504]
 // (8 significant bits fit in 11): the bf16 bits shifted up are the binary32 value, and the
@@ -166,10 +175,42 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const s16x4& lo, const s16x4& hi)
 // scaled by their key's scale; the RoPE part runs on bf16 MFMA with both operands exact.
 template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* qr_lane,
-                                        const typename QFrag<FMT>::type (&qb)[2][8], int kt,
-                                        f32x4 (&sk)[2], int g16, int c16) {
+                                        const typename QFrag<FMT>::type (&qb)[2][QFrag<FMT>::N],
+                                        int kt, f32x4 (&sk)[2], int g16, int c16) {
   using G = MlaGeom<ROPE, FMT>;
   constexpr int RS = G::RS;
+  if constexpr (FMT == kFmtE4m3) {
+    // FP8 x FP8 on v_mfma_scale_f32_16x16x128_f8f6f4: lane (g, i) supplies key 16 kt + i,
+    // bytes 32 g .. 32 g + 31 of each 128-dim chunk.  Half 0 also takes the 64 RoPE dims
+    // (lane groups 2, 3 of that fragment are zero on both sides).  The logit scale
+    // (kv_scale * q_scale * sigma) is applied to the sum by the caller.
+    const unsigned char* krow = raw + (kt * 16 + c16) * RS;
+    i32x8 kf[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + 256 * DH + 128 * i + 32 * g16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + 256 * DH + 128 * i + 32 * g16 + 16);
+      kf[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    if (ROPE && DH == 0) {
+      const unsigned char* kr = krow + G::ROPE_OFF + 32 * (g16 & 1);   // inside the row
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(kr);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + 16);
+      const bool live = g16 < 2;
+      kf[2] = i32x8{live ? (int)lo[0] : 0, live ? (int)lo[1] : 0, live ? (int)lo[2] : 0,
+                    live ? (int)lo[3] : 0, live ? (int)hi[0] : 0, live ? (int)hi[1] : 0,
+                    live ? (int)hi[2] : 0, live ? (int)hi[3] : 0};
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      f32x4 t = mfma_fp8(kf[0], qb[ht][0], f32x4{0.f, 0.f, 0.f, 0.f});
+      t = mfma_fp8(kf[1], qb[ht][1], t);
+      if (ROPE && DH == 0) t = mfma_fp8(kf[2], qb[ht][2], t);
+      sk[ht] = t;
+    }
+    return;
+  } else {
   f32x4 t0[2], t1[2], tr[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
@@ -248,6 +289,7 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
     for (int j = 0; j < 4; ++j)
       sk[ht][j] = fmaf(t1[ht][j], sc[j][1], fmaf(t0[ht][j], sc[j][0], tr[ht][j]));
   }
+  }
 }
 
 // O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.  V^T fragments
@@ -294,10 +336,10 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
 #pragma unroll
   for (int b2 = 0; b2 < 2; ++b2) {
     const int blk = 2 * DH + b2;
-    float vsc[8];
+    float vsc[8];   // per-key scale of this 128-dim block (the per-tensor scale comes later)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      vsc[e] = *reinterpret_cast<const float*>(
+      vsc[e] = FMT == kFmtE4m3 ? 1.0f : *reinterpret_cast<const float*>(
           raw + (16 * (e >> 2) + 4 * g16 + (e & 3)) * RS + kScaleOff + 4 * blk);
     typedef int v2i __attribute__((ext_vector_type(2)));
     auto read_v = [&](int dd) {
@@ -310,11 +352,14 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
     for (int dd = 0; dd < 4; ++dd) vw[dd] = read_v(dd);
     f16x8 pb[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc_bad |= !(fabsf(vsc[e]) <= kMaxVScale);
+    for (int e = 0; e < 8; ++e)
+      if (FMT == kFmtFp8) sc_bad |= !(fabsf(vsc[e]) <= kMaxVScale);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[ht][e] = (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
+      for (int e = 0; e < 8; ++e)
+        pb[ht][e] = FMT == kFmtE4m3 ? (_Float16)pv[ht][e >> 2][e & 3]
+                                    : (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       __builtin_amdgcn_sched_barrier(0);
@@ -391,7 +436,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     slot_sh[i] = slot;
   }
   // RoPE query of the group's heads (bf16, as given) into LDS.
-  if (ROPE) {
+  if (ROPE && FMT != kFmtE4m3) {
     for (int i = tid; i < kHeadsPerWg * 8; i += NT) {
       const int hh = i >> 3, q8 = i & 7;
       u32x4 v = u32x4{0, 0, 0, 0};
@@ -436,11 +481,32 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int g16 = lane0 >> 4, c16 = lane0 & 15;
   const bool ht_live[2] = {h0 < H, h0 + 16 < H};
   const bool active = ht_live[0];
-  typename QFrag<FMT>::type qb[2][8];
+  typename QFrag<FMT>::type qb[2][QFrag<FMT>::N];
   bool q_range = true;
+  float qks[2] = {1.0f, 1.0f};   // logit scale per head (lane column)
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int hq = ht_live[ht] ? h0 + 16 * ht + c16 : c16;
+    if constexpr (FMT == kFmtE4m3) {
+      // E4M3 codes [r][h][512 + ROPE]; value = code * q_scale[r][h].
+      const uint8_t* qh = static_cast<const uint8_t*>(a.q) + ((size_t)r * H + hq) * (512 + ROPE);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        u32x4 lo = u32x4{0, 0, 0, 0}, hi = u32x4{0, 0, 0, 0};
+        const bool live = i < 2 || (ROPE && dh == 0 && g16 < 2);
+        const uint8_t* src = i < 2 ? qh + 256 * dh + 128 * i + 32 * g16 : qh + 512 + 32 * g16;
+        if (live) {
+          lo = *reinterpret_cast<const u32x4*>(src);
+          hi = *reinterpret_cast<const u32x4*>(src + 16);
+        }
+        qb[ht][i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      const float qs = a.q_scale[(size_t)r * H + hq];
+      q_range &= fabsf(qs) <= 3.4028235e38f;   // finite
+      qks[ht] = a.kv_scale * qs;
+      continue;
+    } else {
     const __bf16* qh = static_cast<const __bf16*>(a.q) + ((size_t)r * H + hq) * (512 + ROPE) +
                        256 * dh + 8 * g16;
 #pragma unroll
@@ -457,9 +523,12 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         }
       }
     }
+    }
   }
   if (__any(!q_range) && active && lane0 == 0) raise_fault(a.fault, kFaultRange);
   const float qk_scale = a.softmax_scale * ssmax_mult(a.ssmax_s, row_ok ? p : 0) * kLog2e;
+  qks[0] *= qk_scale;
+  qks[1] *= qk_scale;
 
   f32x4 o_acc[2][16];
 #pragma unroll
@@ -518,7 +587,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
           const f32x4 sum = p0[(2 * kt + ht) * kWave + lane] + p1[(2 * kt + ht) * kWave + lane];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            pv[ht][kt][j] = sv[kt][j] >= 0 ? sum[j] * qk_scale : -__builtin_inff();
+            pv[ht][kt][j] = sv[kt][j] >= 0 ? sum[j] * qks[ht] : -__builtin_inff();
         }
     }
 
@@ -568,7 +637,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     if (!ht_live[ht]) continue;
     const float l = sum_over_lane_groups(l_part[ht]);
     const int h = h0 + 16 * ht + c16e;
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    // Plain E4M3 rows: V's per-tensor scale multiplies the normalised sum.
+    const float inv = l > 0.f ? (FMT == kFmtE4m3 ? a.kv_scale : 1.0f) / l : 0.f;
     const float lse2 = l > 0.f ? m_run[ht] + log2f(l) : -__builtin_inff();
     const int d0 = 256 * dh + 4 * g16e;
     if (nsplit == 1) {
@@ -766,6 +836,9 @@ hipError_t launch_mla(const MlaLaunch& a, hipStream_t st) {
   if (a.bf16_rows)
     e = a.rope_dim ? launch_rows<64, kFmtBf16>(a, pl, part, st)
                    : launch_rows<0, kFmtBf16>(a, pl, part, st);
+  else if (a.e4m3_rows)
+    e = a.rope_dim ? launch_rows<64, kFmtE4m3>(a, pl, part, st)
+                   : launch_rows<0, kFmtE4m3>(a, pl, part, st);
   else
     e = a.rope_dim ? launch_rows<64, kFmtFp8>(a, pl, part, st)
                    : launch_rows<0, kFmtFp8>(a, pl, part, st);

@@ -16,18 +16,18 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ML4DSA_LIB") or os.path.join(PKG, "libml4dsa.so")
 
 # ---- constants mirrored from include/ml4dsa.h
-ML4_ABI_VERSION = 2
+ML4_ABI_VERSION = 3
 ML4_OK, ML4_E_INVALID, ML4_E_UNSUPPORTED, ML4_E_WORKSPACE, ML4_E_LAUNCH, ML4_E_DEVICE_FAULT = (
     0, -1, -2, -3, -4, -5)
 ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
 ML4_IDX_F32, ML4_IDX_FP8_132 = 0, 1
-ML4_LAT_F32, ML4_LAT_FP8_656, ML4_LAT_BF16_1152 = 0, 1, 2
+ML4_LAT_F32, ML4_LAT_FP8_656, ML4_LAT_BF16_1152, ML4_LAT_E4M3_576 = 0, 1, 2, 3
 ML4_FAULT_BLOCK_ID, ML4_FAULT_TOPK_INDEX, ML4_FAULT_NAN_SCORE, ML4_FAULT_QPOS = 1, 2, 4, 8
 ML4_FAULT_RANGE = 16
 ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
-           "ml4_sparse_attn_layer", "ml4_window_mla_decode", "ml4_index_cache_write", "ml4_latent_cache_write",
+           "ml4_sparse_mla_decode_e4m3", "ml4_sparse_attn_layer", "ml4_window_mla_decode", "ml4_index_cache_write", "ml4_latent_cache_write",
            "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
            "ml4_fault_query", "ml4_abi_version")
 
@@ -84,6 +84,10 @@ def _load() -> C.CDLL:
     lib.ml4_sparse_mla_decode.restype = C.c_int
     lib.ml4_sparse_mla_decode.argtypes = [P(ml4_seqs), P(ml4_cache), vp, i32, i32, i32, vp, vp,
                                           i32, f32, f32, vp, i32, vp, vp, sz, vp, vp]
+    lib.ml4_sparse_mla_decode_e4m3.restype = C.c_int
+    lib.ml4_sparse_mla_decode_e4m3.argtypes = [P(ml4_seqs), P(ml4_cache), f32, vp, vp, i32, i32,
+                                               vp, vp, i32, f32, f32, vp, i32, vp, vp, sz, vp,
+                                               vp]
     lib.ml4_sparse_attn_layer.restype = C.c_int
     lib.ml4_sparse_attn_layer.argtypes = [P(ml4_layer), P(ml4_seqs), P(ml4_cache),
                                           P(ml4_cache), i32, vp, i32, vp, vp, vp, i32,
@@ -201,6 +205,18 @@ def ml4_sparse_mla_decode(seqs, kv, q, q_dtype, n_heads, rope_dim, topk_idx, top
                                    rope_dim, ptr(topk_idx), ptr(topk_len), top_k, softmax_scale,
                                    ssmax_s, ptr(out), out_dtype, ptr(lse), ptr(ws), ws_bytes,
                                    ptr(fault), stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_sparse_mla_decode_e4m3(seqs, kv, kv_scale, q, q_scale, n_heads, rope_dim, topk_idx,
+                               topk_len, top_k, softmax_scale, ssmax_s, out, out_dtype,
+                               lse=None, ws=None, ws_bytes=0, fault=None, stream=None,
+                               check=True) -> int:
+    rc = LIB.ml4_sparse_mla_decode_e4m3(C.byref(seqs), C.byref(kv), kv_scale, ptr(q),
+                                        ptr(q_scale), n_heads, rope_dim, ptr(topk_idx),
+                                        ptr(topk_len), top_k, softmax_scale, ssmax_s, ptr(out),
+                                        out_dtype, ptr(lse), ptr(ws), ws_bytes, ptr(fault),
+                                        stream_handle(stream))
     return _check(rc) if check else rc
 
 

@@ -18,7 +18,7 @@ M = pytest.importorskip("sparse_attention_decode_dsa_amd.ml4dsa",
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ml4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ml4_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_bound_entry_points():
@@ -97,6 +97,45 @@ def test_mla_default_deny():
                    "topk_idx and topk_len", "top_k above 2048", "softmax_scale",
                    "ssmax_s must be finite"]:
         assert needle in msg, (needle, msg)
+
+
+def test_e4m3_mla_default_deny():
+    """The plain-E4M3 layout carries scales: the generic entry refuses it, and its own entry
+    checks the format, both scales, the output dtype and the shared MLA arguments."""
+    s = _seqs()
+    rc = M.ml4_sparse_mla_decode(s, _cache(M.ML4_LAT_E4M3_576), 0x7000, M.ML4_FP8_E4M3, 16,
+                                 64, 0x5000, 0x5100, 2048, 0.04, 0.0, 0x8000, M.ML4_BF16,
+                                 stream=0, check=False)
+    assert rc == M.ML4_E_INVALID and "use ml4_sparse_mla_decode_e4m3" in M.ml4_last_error()
+    rc = M.ml4_sparse_mla_decode_e4m3(s, _cache(M.ML4_LAT_FP8_656), float("inf"), 0x7008, None,
+                                      24, 64, 0x5000, 0x5100, 2048, 0.04, 0.0, 0x8000,
+                                      M.ML4_F32, stream=0, check=False)
+    assert rc == M.ML4_E_INVALID
+    msg = M.ml4_last_error()
+    for needle in ["kv.format must be ML4_LAT_E4M3_576", "kv_scale must be finite and > 0",
+                   "q_scale is NULL", "q must be 16-byte aligned",
+                   "n_heads must be a multiple of 16"]:
+        assert needle in msg, (needle, msg)
+    rc = M.ml4_sparse_mla_decode_e4m3(s, _cache(M.ML4_LAT_E4M3_576), 0.01, 0x7000, 0x7100,
+                                      16, 64, 0x5000, 0x5100, 2048, 0.04, 0.0, 0x8000,
+                                      M.ML4_F32, stream=0, check=False)
+    assert rc == M.ML4_E_INVALID
+    assert "ML4_FP8_E4M3 queries and ML4_BF16 outputs" in M.ml4_last_error()
+    # window attention and the fused layer take the other layouts only
+    rc = M.ml4_window_mla_decode(s, _cache(M.ML4_LAT_E4M3_576), 0x7000, M.ML4_FP8_E4M3, 16,
+                                 64, 2048, 0.04, 0.0, 0x8000, M.ML4_BF16, stream=0,
+                                 check=False)
+    assert rc == M.ML4_E_UNSUPPORTED and "window attention" in M.ml4_last_error()
+    L = M.ml4_layer()
+    L.layer, L.kv_sharing_target_layer, L.topk_source_layer = 0, -1, -1
+    L.rope_dim, L.top_k, L.idx_heads, L.mla_heads = 64, 2048, 64, 128
+    L.softmax_scale = 0.04
+    rc = M.ml4_sparse_attn_layer(L, s, [_cache(M.ML4_LAT_E4M3_576)],
+                                 [_cache(M.ML4_IDX_FP8_132)], 0x100, M.ML4_FP8_E4M3, None,
+                                 0x100, 0x100, M.ML4_FP8_E4M3, [0x100], [0x100], 0x100,
+                                 M.ML4_BF16, stream=0, check=False)
+    assert rc in (M.ML4_E_UNSUPPORTED, M.ML4_E_INVALID)
+    assert "ml4_sparse_mla_decode_e4m3" in M.ml4_last_error()
 
 
 def test_layer_modes_are_validated():

@@ -92,3 +92,49 @@ def test_window_mla_matches_oracle(fmt, window, rope):
     ro, rl = O.sparse_mla(batch_np(b), t_np(pool), fmt, t_np(q), rope, idx, ln, 0.04, 0.3)
     check_close(o, ro, "out")
     check_close(lse, rl, "lse")
+
+
+def _run_e4m3(b, pool, kv_scale, q, q_scale, heads, rope, idx, ln, top_k=2048, scale=0.04,
+              ssmax=0.3):
+    bd, pd, qd, qsd = b.to(DEV), pool.to(DEV), q.to(DEV), q_scale.to(DEV)
+    idd, lnd = torch.from_numpy(idx).to(DEV), torch.from_numpy(ln).to(DEV)
+    seqs = M.make_seqs(bd)
+    cache = M.make_cache(pd, M.ML4_LAT_E4M3_576)
+    out = torch.empty(b.total_q, heads, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(b.total_q, heads, dtype=torch.float32, device=DEV)
+    fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_MLA, seqs, heads, top_k)
+    ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=DEV)
+    M.ml4_sparse_mla_decode_e4m3(seqs, cache, kv_scale, qd, qsd, heads, rope, idd, lnd, top_k,
+                                 scale, ssmax, out, M.ML4_BF16, lse, ws, wsn, fault)
+    torch.cuda.synchronize()
+    f = M.ml4_fault_query(fault)
+    del bd, pd, qd, qsd, idd, lnd
+    return O.decode_bf16(t_np(out)), t_np(lse), f
+
+
+@pytest.mark.parametrize("heads,rope,top_k", [(128, 64, 2048), (64, 0, 2048), (16, 64, 2048),
+                                              (32, 0, 100)])
+def test_e4m3_rows_sparse_mla_matches_oracle(heads, rope, top_k):
+    """Plain E4M3 rows with a per-tensor scale and FP8 queries (QK on FP8 MFMA)."""
+    print(f"[gpu] e4m3 rows H={heads} rope={rope} k={top_k}", flush=True)
+    b = synth.make_batch(11 + heads, [3000, 700, 2100], [2, 1, 3], 64, extra_blocks=3)
+    pool, kv_scale = synth.make_plain_e4m3_pool(12 + heads, b.num_blocks, 64)
+    q, qs = synth.make_mla_query_fp8(13 + heads, b.total_q, heads, rope)
+    idx, ln = _sel(b.q_pos.numpy(), top_k, heads)
+    o, lse, f = _run_e4m3(b, pool, kv_scale, q, qs, heads, rope, idx, ln, top_k)
+    assert f == 0
+    ro, rl = O.sparse_mla(batch_np(b), t_np(pool), "e4m3", t_np(q), rope, idx, ln, 0.04, 0.3,
+                          q_scale=t_np(qs), kv_scale=kv_scale)
+    check_close(o, ro, "out")
+    check_close(lse, rl, "lse")
+
+
+def test_e4m3_rows_non_finite_query_scale_is_reported():
+    b = synth.make_batch(3, [500], [2], 64, extra_blocks=1)
+    pool, kv_scale = synth.make_plain_e4m3_pool(4, b.num_blocks, 64)
+    q, qs = synth.make_mla_query_fp8(5, b.total_q, 16, 64)
+    qs[1, 3] = float("nan")
+    idx, ln = _sel(b.q_pos.numpy(), 64, 1)
+    _, _, f = _run_e4m3(b, pool, kv_scale, q, qs, 16, 64, idx, ln, 64)
+    assert f == M.ML4_FAULT_RANGE
