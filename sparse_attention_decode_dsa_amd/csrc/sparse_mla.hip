@@ -11,8 +11,8 @@
 // One work-group = one query row x up to 128 heads x a contiguous range of its selected
 // keys, 8 waves.  Per 32-key tile:
 //   gather  the selected 656-byte rows (slot = block_table[t / bs] * bs + t % bs) straight
-//           into an LDS ring with 16-byte global->LDS transfers, up to three tiles ahead of
-//           the math; the rows keep the cache layout and are never rewritten;
+//           into a three-tile LDS ring with 16-byte global->LDS transfers, issued two tiles
+//           ahead of the math; the rows keep the cache layout and are never rewritten;
 //   QK      S^T = K . Q^T with keys on M and heads on N.  Latent K fragments are read as
 //           e4m3 and decoded exactly to fp16 in registers for v_mfma_f32_16x16x32_f16 (the
 //           bf16 query is rounded to fp16, a value beyond its range is reported); each wave
@@ -29,6 +29,8 @@
 //           and the per-128 scale of V is folded into P per column block.  fp16 keeps 11
 //           significant bits of P, which bounds the output error by 2^-11 * sum_t p_t |c_t|
 //           even when SSMax makes the softmax peaked.
+// One work-group barrier per tile: after QK the waves wait for the next tile's transfers,
+// so the barrier that publishes the partial S also publishes the next tile.
 // A row's selected keys may be split across work-groups; the partial results are merged by
 // their log-sum-exp in a second kernel.
 #include "ml4_device.h"
@@ -38,7 +40,8 @@ namespace ml4 {
 namespace {
 
 constexpr int kTK = 32;            // keys per tile
-constexpr int kQRS = 72;           // bf16 stride of a head's RoPE query in LDS (64 + 8)
+constexpr int kQRS = 80;           // bf16 stride of a head's RoPE query in LDS (64 + 16:
+                                   // conflict-free 16-byte reads)
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kMaxVScale = 128.0f;   // 2^8 * 128 * 448 stays inside fp16 after P * scale
 constexpr uint32_t kFaultBlock = 1u << 0;
@@ -47,7 +50,6 @@ constexpr uint32_t kFaultQpos = 1u << 3;
 constexpr uint32_t kFaultRange = 1u << 4;
 
 
-constexpr int kNStage = 4;         // gather ring: the tile being read + up to three in flight
 
 // Source of the gather for masked keys and for lanes past the end of a tile.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
@@ -98,8 +100,7 @@ __device__ __forceinline__ float sum_over_lane_groups(float v) {
 // tile's rows sit at a stride of RS = 16 NCH bytes with the cache row's own layout, and the
 // matrix-core operands are read from there directly.
 //   FMT kFmtFp8:  fp8_ds_mla rows, [512 e4m3][4 x fp32 scale][64 x bf16 RoPE] = 656 B;
-//   FMT kFmtBf16: bf16 rows, [512 x bf16][64 x bf16 RoPE] = 1,152 B (four-tile ring does not
-//                 fit; two tiles, one in flight);
+//   FMT kFmtBf16: bf16 rows, [512 x bf16][64 x bf16 RoPE] = 1,152 B (a two-tile ring);
 //   FMT kFmtE4m3: plain E4M3 rows, [512 x e4m3][64 x e4m3 RoPE] = 576 B, one per-tensor scale.
 //                 A NoPE layer gathers 33 chunks (528 B) per row: the padding chunk (RoPE
 //                 bytes, never read) keeps rows off a 512-B LDS stride.
@@ -112,7 +113,12 @@ struct MlaGeom {
   static constexpr int ROPE_OFF = FMT == kFmtFp8 ? 528 : FMT == kFmtBf16 ? 1024 : 512;
   static constexpr int NCH =                                        // 16-B chunks read per row
       ROPE ? ROW_BYTES / 16 : FMT == kFmtE4m3 ? 33 : ROPE_OFF / 16;
-  static constexpr int NSTAGE = FMT == kFmtFp8 ? kNStage : 2;
+  // One barrier per tile (fp8_ds_mla and plain E4M3 rows): a three-tile ring and two
+  // partial-S buffers, so that the barrier after QK also publishes the next tile.  The bf16 rows do not fit that and
+  // keep two barriers per tile over a two-tile ring.
+  static constexpr bool ONEBAR = FMT != kFmtBf16;
+  static constexpr int NSTAGE = ONEBAR ? 3 : 2;
+  static constexpr int XS_BUFS = ONEBAR ? 2 : 1;
   static constexpr int RS = 16 * NCH;                   // bytes per gathered row
   static constexpr int RAW = kTK * NCH;                 // chunks per tile
   static constexpr int NBLK = (RAW + kWave - 1) / kWave;
@@ -120,7 +126,8 @@ struct MlaGeom {
   static constexpr int STAGE = NBLK * 1024;
   static constexpr int OFF_JUNK = NSTAGE * STAGE;
   static constexpr int OFF_XS = OFF_JUNK + 1024;                      // [8][4][64] f32x4
-  static constexpr int OFF_QR = OFF_XS + kMlaWaves * 4 * kWave * 16;  // [128][kQRS] bf16
+  static constexpr int XS_WORDS = kMlaWaves * 4 * kWave;            // f32x4 per buffer
+  static constexpr int OFF_QR = OFF_XS + XS_BUFS * XS_WORDS * 16;    // [128][kQRS] bf16
   static constexpr int OFF_SLOT = OFF_QR + (ROPE && FMT != kFmtE4m3 ? kHeadsPerWg * kQRS * 2 : 0);
   static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
 };
@@ -251,15 +258,19 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
     return;
   }
   if constexpr (FMT == kFmtFp8) {
-  const unsigned char* krow = raw + (kt * 16 + c16) * RS + 256 * DH + 8 * g16;
-  u32x2 kw[8];
+  // Key c of sub-tile kt sits in LDS row 2c + kt; lane (g, c) reads 16 bytes per pair of
+  // k-steps (dims 64 jj + 16 g .. +15 of the half).  Both choices make every half-wave's
+  // 16-byte reads hit distinct bank groups.
+  const unsigned char* krow = raw + (2 * c16 + kt) * RS + 256 * DH + 16 * g16;
+  u32x4 kw[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kw[i] = *reinterpret_cast<const u32x2*>(krow + 32 * i);
+  for (int jj = 0; jj < 4; ++jj) kw[jj] = *reinterpret_cast<const u32x4*>(krow + 64 * jj);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    const u32x2 w = kw[i];
-    const f16x4 lo = e4m3x4_to_f16(w[0]), hi = e4m3x4_to_f16(w[1]);
+    const u32x4 w = kw[i >> 1];
+    const f16x4 lo = e4m3x4_to_f16((i & 1) ? w[2] : w[0]);
+    const f16x4 hi = e4m3x4_to_f16((i & 1) ? w[3] : w[1]);
     const f16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     if (i < 4) {
       t0[0] = mfma_f16(k, qb[0][i], t0[0]);
@@ -272,16 +283,16 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
   __builtin_amdgcn_sched_barrier(0);
   if (ROPE) {
     const bf16x8 kr = *reinterpret_cast<const bf16x8*>(
-        raw + (kt * 16 + c16) * RS + G::ROPE_OFF + 2 * (32 * DH + 8 * g16));
+        raw + (2 * c16 + kt) * RS + G::ROPE_OFF + 2 * (32 * DH + 8 * g16));
     const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
     const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
     tr[0] = mfma_bf16(kr, q0, tr[0]);
     tr[1] = mfma_bf16(kr, q1, tr[1]);
   }
-  f32x2 sc[4];
+  f32x2 sc[4];   // scales of keys 4 g + j of the sub-tile (LDS rows 2 (4 g + j) + kt)
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    sc[j] = *reinterpret_cast<const f32x2*>(raw + (kt * 16 + 4 * g16 + j) * RS + kScaleOff +
+    sc[j] = *reinterpret_cast<const f32x2*>(raw + (2 * (4 * g16 + j) + kt) * RS + kScaleOff +
                                             8 * DH);
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
@@ -294,9 +305,9 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
 
 // O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.  V^T fragments
 // come straight from the e4m3 rows through ds_read_b64_tr_b8: in lane group g, lane pair
-// (2e, 2e+1) addresses row kp(g, e) = 16 (e >> 2) + 4 g + (e & 3) (bytes 8 (lane & 1) of the
-// fragment's 16 dims), and lane (g, i) receives dim i of rows kp(g, 0..7) -- the key order of
-// the P^T operand taken from the S^T accumulators in place.
+// (2e, 2e+1) addresses the LDS row of key 4 g + (e & 3) of sub-tile e >> 2 (bytes 8 (lane & 1)
+// of the fragment's 16 dims), and lane (g, i) receives dim i of those eight rows -- the key
+// order of the P^T operand taken from the S^T accumulators in place.
 template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&pv)[2][2][4],
                                         f32x4 (&o_acc)[2][16], bool& sc_bad, int g16,
@@ -330,8 +341,12 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
     (void)sc_bad;
     return;
   } else {
+  // LDS row of P^T's K-index e in lane group g: key 4 g + (e & 3) of sub-tile e >> 2.
+  auto kp_row = [&](int e) {
+    return FMT == kFmtFp8 ? 2 * (4 * g16 + (e & 3)) + (e >> 2) : 16 * (e >> 2) + 4 * g16 + (e & 3);
+  };
   const int e2 = c16 >> 1;
-  const int kp = 16 * (e2 >> 2) + 4 * g16 + (e2 & 3);
+  const int kp = kp_row(e2);
   const unsigned char* vbase = raw + kp * RS + 256 * DH + 8 * (c16 & 1);
 #pragma unroll
   for (int b2 = 0; b2 < 2; ++b2) {
@@ -340,7 +355,7 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vsc[e] = FMT == kFmtE4m3 ? 1.0f : *reinterpret_cast<const float*>(
-          raw + (16 * (e >> 2) + 4 * g16 + (e & 3)) * RS + kScaleOff + 4 * blk);
+          raw + kp_row(e) * RS + kScaleOff + 4 * blk);
     typedef int v2i __attribute__((ext_vector_type(2)));
     auto read_v = [&](int dd) {
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -508,10 +523,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       continue;
     } else {
     const __bf16* qh = static_cast<const __bf16*>(a.q) + ((size_t)r * H + hq) * (512 + ROPE) +
-                       256 * dh + 8 * g16;
+                       256 * dh;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * i);
+      // k-step i's dims: fp8_ds_mla rows pair k-steps in 16-byte reads (dims 64 (i/2) +
+      // 16 g + 8 (i%2) ..), bf16 rows take dims 32 i + 8 g ..
+      const int qo = FMT == kFmtFp8 ? 64 * (i >> 1) + 16 * g16 + 8 * (i & 1) : 32 * i + 8 * g16;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + qo);
       if constexpr (FMT == kFmtBf16) {
         qb[ht][i] = v;                   // bf16 rows: bf16 MFMA, the query as given
       } else {
@@ -539,9 +557,17 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   float l_part[2] = {0.f, 0.f};
   bool sc_bad = false;   // a latent scale that could push P * scale out of fp16
 
+  if constexpr (G::ONEBAR) {
+    if (ntiles > 0) issue(0, lane0);
+    if (ntiles > 1) issue(1, lane0);
+    if (ntiles > 1) wait_vmcnt<G::PER_WAVE>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // tile 0 is in LDS
+  } else {
 #pragma unroll
-  for (int t = 0; t < G::NSTAGE - 1; ++t)
-    if (t < ntiles) issue(t, lane0);
+    for (int t = 0; t < G::NSTAGE - 1; ++t)
+      if (t < ntiles) issue(t, lane0);
+  }
   for (int tile = 0; tile < ntiles; ++tile) {
     // Lane-derived addresses are recomputed every tile (a few VALU instructions) rather than
     // hoisted out of the loop: the query and the accumulator leave no registers to keep them.
@@ -549,19 +575,20 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, c16 = lane & 15;
     const unsigned char* raw = smem + (tile % G::NSTAGE) * G::STAGE;
-    // This tile's transfers are the oldest outstanding ones: later tiles may stay in flight.
-    const int ahead = min(G::NSTAGE - 2, ntiles - 1 - tile);
-    if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
-    else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
-    else wait_vmcnt<0>();
-    __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
-    if (tile + G::NSTAGE - 1 < ntiles) issue(tile + G::NSTAGE - 1, lane);
+    if constexpr (!G::ONEBAR) {
+      // Two-tile ring: this tile's transfers are the only outstanding ones.
+      static_assert(G::NSTAGE == 2, "the wait below assumes one tile in flight");
+      wait_vmcnt<0>();
+      __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
+      if (tile + G::NSTAGE - 1 < ntiles) issue(tile + G::NSTAGE - 1, lane);
+    }
+    f32x4* xsb = xs + (G::ONEBAR ? (tile & 1) * G::XS_WORDS : 0);
 
     // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
     //      partner waves then add half 0 + half 1 in the same order
     {
       const __bf16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
-      f32x4* mine = xs + wave * 4 * kWave;
+      f32x4* mine = xsb + wave * 4 * kWave;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 sk[2];
@@ -571,15 +598,28 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         mine[(2 * kt + 1) * kWave + lane] = sk[1];
       }
     }
-    __syncthreads();
+    if constexpr (G::ONEBAR) {
+      // Only tile + 1's transfers are outstanding.  After the barrier every wave's partial
+      // S of this tile and tile + 1 are in LDS, and every wave is done with tile - 1, whose
+      // ring slot takes tile + 2.
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tile + 2 < ntiles) issue(tile + 2, lane);
+    } else {
+      __syncthreads();
+    }
     float pv[2][2][4];
     {
-      const f32x4* p0 = xs + hg * 4 * kWave;
-      const f32x4* p1 = xs + (hg | 4) * 4 * kWave;
-      const int* sl = slot_sh + tile * kTK + 4 * g16;
+      const f32x4* p0 = xsb + hg * 4 * kWave;
+      const f32x4* p1 = xsb + (hg | 4) * 4 * kWave;
+      // slots of accumulator keys (kt, 4 g + j): selection index 8 g + 2 j + kt with the
+      // interleaved rows of fp8_ds_mla tiles, 16 kt + 4 g + j otherwise
+      constexpr bool IL = FMT == kFmtFp8;
+      const int* sl = slot_sh + tile * kTK + (IL ? 8 : 4) * g16;
       const int4 s0 = *reinterpret_cast<const int4*>(sl);
-      const int4 s1 = *reinterpret_cast<const int4*>(sl + 16);
-      const int sv[2][4] = {{s0.x, s0.y, s0.z, s0.w}, {s1.x, s1.y, s1.z, s1.w}};
+      const int4 s1 = *reinterpret_cast<const int4*>(sl + (IL ? 4 : 16));
+      const int sv[2][4] = {{IL ? s0.x : s0.x, IL ? s0.z : s0.y, IL ? s1.x : s0.z, IL ? s1.z : s0.w},
+                            {IL ? s0.y : s1.x, IL ? s0.w : s1.y, IL ? s1.y : s1.z, IL ? s1.w : s1.w}};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
