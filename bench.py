@@ -354,6 +354,7 @@ def main():
                "mla": sum(p["mla_us"] for p in per.values())}
         dom = max(tot, key=tot.get)
         l0 = layers[0]
+        rope0 = case.layers[0]["rope_dim"]
         # The bound is the resource whose time floor is larger for this kernel's work.
         if dom == "indexer":
             us = per[l0]["indexer_us"]
@@ -376,7 +377,8 @@ def main():
                     "frac": ach / PEAK_HBM_GBS}
         roof["algorithmic_bytes"] = nbytes
         roof["algorithmic_flops"] = flops
-        roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8", "topk": "k_topk_row"}[dom]
+        roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8<%d, 0>" % rope0,
+                          "topk": "k_topk_cand"}[dom]
         roof["layer"] = l0
         roof["avg_launch_us"] = us
         roof["traffic"] = load_traffic(dom)

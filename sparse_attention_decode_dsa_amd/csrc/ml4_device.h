@@ -103,4 +103,17 @@ __device__ __forceinline__ int request_of(const int32_t* q_start, int batch, int
   return lo;
 }
 
+// The same, found by a whole wave in one round of loads (every lane passes the same r):
+// q_start is non-decreasing, so the owner is the number of b in [1, batch) with
+// q_start[b] <= r.
+__device__ __forceinline__ int request_of_wave(const int32_t* q_start, int batch, int r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int n = 0;
+  for (int base = 1; base < batch; base += kWave) {
+    const int i = base + lane;
+    n += __popcll(__ballot(i < batch && q_start[i] <= r));
+  }
+  return n;
+}
+
 }  // namespace ml4

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int split = blockIdx.z;
   const SeqView& s = a.s;
   const int H = a.n_heads;
-  const int b = request_of(s.q_start, s.batch, r);
+  const int b = request_of_wave(s.q_start, s.batch, r);
   const int p = s.q_pos[r];
   bool row_ok = true;
   if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len) {

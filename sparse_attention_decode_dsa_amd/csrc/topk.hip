@@ -97,7 +97,7 @@ __device__ void find_digit(const uint32_t* hist, int nb, int need, int* out, int
 
 __device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_out) {
   const SeqView& s = a.s;
-  const int b = request_of(s.q_start, s.batch, r);
+  const int b = request_of_wave(s.q_start, s.batch, r);
   const int p = s.q_pos[r];
   int32_t* out = a.idx + (size_t)r * a.top_k;
   if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len || (int64_t)p >= a.ld) {
