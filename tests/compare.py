@@ -67,7 +67,8 @@ def check_close(gpu, ref, what, atol=ATOL, rtol=RTOL):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_inf = np.isinf(ref) & (gpu == ref)
-    err = np.abs(gpu - ref)
+    with np.errstate(invalid="ignore"):      # inf - inf where both sides are the same inf
+        err = np.where(both_inf, 0.0, np.abs(gpu - ref))
     bound = atol + rtol * np.abs(ref)
     bad = ~(both_inf | (err <= bound))
     if bad.any():

@@ -138,3 +138,63 @@ def test_e4m3_rows_non_finite_query_scale_is_reported():
     idx, ln = _sel(b.q_pos.numpy(), 64, 1)
     _, _, f = _run_e4m3(b, pool, kv_scale, q, qs, 16, 64, idx, ln, 64)
     assert f == M.ML4_FAULT_RANGE
+
+
+def _edge_batch(seed):
+    # request 1 has no query rows; request 3's only row sits at position 0
+    return synth.make_batch(seed, [3000, 50, 7, 1], [6, 0, 2, 1], 64, extra_blocks=2)
+
+
+def _edge_sel(q_pos, top_k, seed):
+    """Selection lengths 0, k, k-1, 33, 32, 31 (tile tails and an empty row), then the
+    visible maximum for the short requests."""
+    g = np.random.default_rng(seed)
+    want = [0, top_k, top_k - 1, 33, 32, 31, 6, 1, 1]
+    idx = np.full((len(q_pos), top_k), -1, dtype=np.int32)
+    ln = np.zeros(len(q_pos), dtype=np.int32)
+    for r, p in enumerate(q_pos):
+        n = min(want[r], int(p) + 1, top_k)
+        idx[r, :n] = np.sort(g.choice(int(p) + 1, size=n, replace=False))
+        ln[r] = n
+    return idx, ln
+
+
+@pytest.mark.parametrize("fmt,heads,rope", [("fp8", 128, 64), ("fp8", 32, 0), ("bf16", 128, 64),
+                                            ("e4m3", 128, 64), ("e4m3", 16, 0)])
+def test_empty_ragged_and_tile_boundary_selections(fmt, heads, rope):
+    """Rows with no selected key (o = 0, lse = -inf), selections ending on and either side
+    of a 32-key tile, k and k - 1, an empty request, and a query at position 0."""
+    print(f"[gpu] edge selections {fmt} H={heads} rope={rope}", flush=True)
+    b = _edge_batch(21)
+    idx, ln = _edge_sel(b.q_pos.numpy(), 2048, 3)
+    assert ln[0] == 0 and ln[1] == 2048 and b.q_pos[-1] == 0
+    if fmt == "e4m3":
+        pool, kv_scale = synth.make_plain_e4m3_pool(22, b.num_blocks, 64)
+        q, qs = synth.make_mla_query_fp8(23, b.total_q, heads, rope)
+        o, lse, f = _run_e4m3(b, pool, kv_scale, q, qs, heads, rope, idx, ln)
+        assert f == 0
+        ro, rl = O.sparse_mla(batch_np(b), t_np(pool), "e4m3", t_np(q), rope, idx, ln, 0.04,
+                              0.3, q_scale=t_np(qs), kv_scale=kv_scale)
+    else:
+        pool = synth.make_latent_pool(22, b.num_blocks, 64, fmt)
+        q = synth.make_mla_query(23, b.total_q, heads, rope, "fp8")
+        o, lse = _run_mla(b, pool, q, fmt, heads, rope, idx, ln)
+        ro, rl = O.sparse_mla(batch_np(b), t_np(pool), fmt, t_np(q), rope, idx, ln, 0.04, 0.3)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    check_close(o, ro, "out")
+    check_close(lse, rl, "lse")
+
+
+@pytest.mark.parametrize("fmt,window", [("fp8", 1), ("bf16", 1), ("fp8", 33), ("bf16", 2047)])
+def test_window_edges(fmt, window):
+    """Window of one key (the query's own), a window one past a tile, and k - 1; rows near
+    the start of their request see fewer keys than the window."""
+    print(f"[gpu] window edges {fmt} W={window}", flush=True)
+    b = _edge_batch(31)
+    pool = synth.make_latent_pool(32, b.num_blocks, 64, fmt)
+    q = synth.make_mla_query(33, b.total_q, 128, 64, "fp8")
+    o, lse = _run_mla(b, pool, q, fmt, 128, 64, window=window)
+    idx, ln = O.window_positions(b.q_pos.numpy(), window)
+    ro, rl = O.sparse_mla(batch_np(b), t_np(pool), fmt, t_np(q), 64, idx, ln, 0.04, 0.3)
+    check_close(o, ro, "out")
+    check_close(lse, rl, "lse")
