@@ -425,13 +425,24 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
   if (tid == 0) { sh_count = 0; sh_nan = 0; }
   __syncthreads();
   bool any_nan = false;
+  // The next batch's loads are issued before the current one is filtered.
+  f32x4 cur[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) cur[u] = first[u];
   for (int base = tid; base - tid < n4; base += kRowThreads * kU) {
+    f32x4 nxt[kU];
+    const int nb = base + kRowThreads * kU;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i4 = nb + u * kRowThreads;
+      nxt[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(row + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     uint32_t kv[kU][4];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i4 = base + u * kRowThreads;
       if (i4 < n4) {
-        const f32x4 v = base == tid ? first[u] : *reinterpret_cast<const f32x4*>(row + 4 * i4);
+        const f32x4 v = cur[u];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bool nn = false;
@@ -464,6 +475,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
           ++slot;
         }
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
   }
   if (any_nan) sh_nan = 1;
   __syncthreads();
