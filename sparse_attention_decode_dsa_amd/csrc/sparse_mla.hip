@@ -832,7 +832,10 @@ MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
   MlaPlan pl{};
   pl.groups = (H + kHeadsPerWg - 1) / kHeadsPerWg;
   const long long base = (long long)s.total_q * pl.groups;
-  const int max_split = max(1, (top_k + 2 * kTK - 1) / (2 * kTK));   // >= 2 tiles per split
+  // >= 4 tiles per split: below that the partials (2 KB per row, head and split, written
+  // and read back) and each split's copy of the row's queries outweigh the extra CUs
+  // (8 decode rows: 56 -> 44 us against 2-tile splits).
+  const int max_split = max(1, (top_k + 4 * kTK - 1) / (4 * kTK));
   int ns = 1;
   while (ns < max_split && base * ns < 256) ns <<= 1;
   ns = min(ns, max_split);
