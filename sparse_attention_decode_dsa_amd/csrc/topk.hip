@@ -572,6 +572,32 @@ __device__ __forceinline__ BigWs big_ws(void* ws, int rows, int chunks) {
   return w;
 }
 
+// Keys lo + 16 i .. lo + 16 i + 15 of the row into thread i's registers, four 16-byte loads
+// in flight at once (a chunk is kBigThreads x 16 keys); bit e of *valid marks key e < hi.
+static_assert(kBigChunk == 16 * kBigThreads, "one 16-key run per thread");
+__device__ __forceinline__ void load_run16(const float* row, int lo, int hi, uint32_t (&k)[16],
+                                           uint32_t* valid, bool* any_nan) {
+  const int t0 = lo + 16 * (int)threadIdx.x;
+  f32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)   // t0 + 4j < hi <= ld, a multiple of 4: the whole vector is in the row
+    v[j] = t0 + 4 * j < hi ? *reinterpret_cast<const f32x4*>(row + t0 + 4 * j)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t ok = 0u;
+  bool nan = false;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    bool nn = false;
+    k[e] = order_key(v[e >> 2][e & 3], nn);
+    if (t0 + e < hi) {
+      ok |= 1u << e;
+      nan |= nn;
+    }
+  }
+  *valid = ok;
+  *any_nan = nan;
+}
+
 __global__ __launch_bounds__(kBigThreads) void k_tkb_init(TopkLaunch a, int chunks) {
   const int r = blockIdx.x;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
@@ -592,26 +618,34 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chu
   const int n = a.s.q_pos[r] + 1;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
   if (lo >= hi) return;
+  __shared__ uint32_t sh_and[kBigThreads / kWave], sh_or[kBigThreads / kWave];
+  __shared__ int sh_nan;
   const float* row = a.scores + (size_t)r * a.ld;
+  uint32_t k[16], valid;
+  bool any_nan;
+  load_run16(row, lo, hi, k, &valid, &any_nan);
   uint32_t av = ~0u, ov = 0u;
-  bool any_nan = false;
-  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
-    bool nn = false;
-    const uint32_t k = order_key(row[t], nn);
-    any_nan |= nn;
-    av &= k;
-    ov |= k;
-  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((valid >> e) & 1u) {
+      av &= k[e];
+      ov |= k[e];
+    }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     av &= (uint32_t)__shfl_xor((int)av, m);
     ov |= (uint32_t)__shfl_xor((int)ov, m);
   }
-  const bool wave_nan = __any(any_nan);
-  if ((threadIdx.x & (kWave - 1)) == 0) {
+  if (threadIdx.x == 0) sh_nan = 0;
+  __syncthreads();
+  if (any_nan) sh_nan = 1;
+  if ((threadIdx.x & (kWave - 1)) == 0) { sh_and[threadIdx.x >> 6] = av; sh_or[threadIdx.x >> 6] = ov; }
+  __syncthreads();
+  if (threadIdx.x == 0) {   // one set of atomics per work-group
+    for (int i = 1; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
     atomicAnd(&w.st[r].and_v, av);
     atomicOr(&w.st[r].or_v, ov);
-    if (wave_nan) atomicOr(&w.st[r].nan, 1u);
+    if (sh_nan) atomicOr(&w.st[r].nan, 1u);
   }
 }
 
@@ -640,11 +674,13 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chun
   for (int i = threadIdx.x; i < nb; i += kBigThreads) hist[i] = 0u;
   __syncthreads();
   const float* row = a.scores + (size_t)r * a.ld;
-  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
-    bool nn = false;
-    const uint32_t k = order_key(row[t], nn);
-    if (digit_prefix(k, s.shift) == s.P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
-  }
+  uint32_t k[16], valid;
+  bool any_nan;
+  load_run16(row, lo, hi, k, &valid, &any_nan);
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (((valid >> e) & 1u) && digit_prefix(k[e], s.shift) == s.P)
+      atomicAdd(&hist[(k[e] >> nsh) & (nb - 1)], 1u);
   __syncthreads();
   uint32_t* g = w.hist + (size_t)r * (1 << kMaxDigitBits);
   for (int i = threadIdx.x; i < nb; i += kBigThreads)
@@ -684,11 +720,17 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chu
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
   const float* row = a.scores + (size_t)r * a.ld;
   int gt = 0, eq = 0;
-  for (int t = lo + threadIdx.x; t < hi; t += kBigThreads) {
-    bool nn = false;
-    const uint64_t h = digit_prefix(order_key(row[t], nn), shift);
-    gt += h > P;
-    eq += h == P;
+  if (lo < hi) {
+    uint32_t k[16], valid;
+    bool any_nan;
+    load_run16(row, lo, hi, k, &valid, &any_nan);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((valid >> e) & 1u) {
+        const uint64_t h = digit_prefix(k[e], shift);
+        gt += h > P;
+        eq += h == P;
+      }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) { gt += __shfl_xor(gt, m); eq += __shfl_xor(eq, m); }
@@ -743,23 +785,36 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chu
   const int K = a.top_k;
   const float* row = a.scores + (size_t)r * a.ld;
   int32_t* out = a.idx + (size_t)r * a.top_k;
-  for (int base = lo; base < hi; base += kBigThreads) {
-    const int t = base + threadIdx.x;
-    bool gt = false, eq = false;
-    if (t < hi) {
-      bool nn = false;
-      const uint64_t h = digit_prefix(order_key(row[t], nn), shift);
-      gt = h > P;
-      eq = h == P;
+  // Thread i owns positions lo + 16 i .. +15, so thread order is position order: one scan
+  // ranks the equal keys, a second places the kept positions.
+  uint32_t k[16], valid;
+  bool any_nan;
+  load_run16(row, lo, hi, k, &valid, &any_nan);
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((valid >> e) & 1u) {
+      const uint64_t h = digit_prefix(k[e], shift);
+      gt |= (h > P ? 1u : 0u) << e;
+      eq |= (h == P ? 1u : 0u) << e;
     }
-    int tot_eq, tot_sel;
-    const int eq_rank = carry_eq + block_exclusive_scan<kBigThreads>(eq ? 1 : 0, &tot_eq, sh_scan);
-    const bool sel = gt || (eq && eq_rank < s.need);
-    const int at = carry_out + block_exclusive_scan<kBigThreads>(sel ? 1 : 0, &tot_sel, sh_scan);
-    if (sel && at < K) out[at] = t;
-    carry_eq += tot_eq;
-    carry_out += tot_sel;
-  }
+  int tot;
+  int eq_rank = carry_eq + block_exclusive_scan<kBigThreads>(__builtin_popcount(eq), &tot, sh_scan);
+  uint32_t sel = gt;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((eq >> e) & 1u) {
+      if (eq_rank < s.need) sel |= 1u << e;
+      ++eq_rank;
+    }
+  int at = carry_out + block_exclusive_scan<kBigThreads>(__builtin_popcount(sel), &tot, sh_scan);
+  const int t0 = lo + 16 * (int)threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((sel >> e) & 1u) {
+      if (at < K) out[at] = t0 + e;
+      ++at;
+    }
 }
 
 
