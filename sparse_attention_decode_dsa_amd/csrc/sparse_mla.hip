@@ -634,6 +634,15 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     // ---- online softmax (base 2) per head (lane column), identical in both partner waves
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
+      // The weights are taken against the running maximum before the tile's own maximum is
+      // known (the two are independent); only when the tile raises the maximum by more
+      // than the slack -- rare after the first tile -- are they taken again.
+      const float msub0 = (m_run[ht] == -__builtin_inff()) ? 0.f : m_run[ht];
+      float ev[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ev[kt][j] = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub0);
       float mt = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -648,16 +657,19 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
         for (int i = 0; i < 16; ++i) o_acc[ht][i] *= alpha;
         m_run[ht] = m_new;
+        // With no finite logit yet every value is -inf and exp2(-inf - 0) = 0.
+        const float msub = (m_new == -__builtin_inff()) ? 0.f : m_new;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ev[kt][j] = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub);
       }
-      // With no finite logit yet every value is -inf and exp2(-inf - 0) = 0.
-      const float msub = (m_run[ht] == -__builtin_inff()) ? 0.f : m_run[ht];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float e = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub);
-          pv[ht][kt][j] = e;
-          l_part[ht] += e;
+          pv[ht][kt][j] = ev[kt][j];
+          l_part[ht] += ev[kt][j];
         }
     }
     __builtin_amdgcn_sched_barrier(0);
