@@ -82,7 +82,8 @@ enum ml4_fault_bits {
   ML4_FAULT_QPOS = 1u << 3,        /* q_pos outside [0, seq_len) or > max_seq_len - 1      */
   ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a bf16 latent-query element beyond the fp16
                                       range (|x| > 65504) or NaN, or a selected key's latent
-                                      scale with |s| > 128 or NaN; that row's output is
+                                      scale with |s| > 128 or NaN; plain-E4M3 MLA: a
+                                      non-finite query scale; that row's output is
                                       unspecified                                          */
 };
 
@@ -160,17 +161,21 @@ int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, i
  *     sigma_r = softmax_scale * (ssmax_s > 0 ? ssmax_s * ln(q_pos[r] + 1) : 1),
  *     out[r][h] = sum_t softmax(l)_t * c_t   (the latent row is key and value),
  *     lse[r][h] = natural-log log-sum-exp of l (or -inf when topk_len[r] == 0, out = 0).
- *   kv       the latent cache to read: the layer's own, or the target's for a consumer.
- *   q        [total_q][n_heads][512 + rope_dim]: bf16 with ML4_LAT_FP8_656, fp32 with
- *            ML4_LAT_F32.   n_heads: multiple of 16, 16 .. 128.   rope_dim: 64, or 0 (NoPE:
- *            the RoPE bytes are never read).
- *   out      [total_q][n_heads][512]: bf16 (fp8 cache) or fp32 (fp32 cache).   lse: fp32
- *            [total_q][n_heads] or NULL.
+ *   kv       the latent cache to read: the layer's own, or the target's for a consumer;
+ *            ML4_LAT_FP8_656, ML4_LAT_BF16_1152 or ML4_LAT_F32 (an ML4_LAT_E4M3_576 cache
+ *            carries scales and goes through ml4_sparse_mla_decode_e4m3).
+ *   q        [total_q][n_heads][512 + rope_dim]: bf16 (ML4_BF16) with ML4_LAT_FP8_656 and
+ *            ML4_LAT_BF16_1152, fp32 with ML4_LAT_F32.   n_heads: multiple of 16, 16 .. 128.
+ *            rope_dim: 64, or 0 (NoPE: the RoPE bytes are never read).
+ *   out      [total_q][n_heads][512]: bf16 (ML4_BF16) for the fp8 and bf16 caches, fp32 for
+ *            the fp32 cache.   lse: fp32 [total_q][n_heads] or NULL.
  *   ws       ml4_workspace_bytes(ML4_ENTRY_MLA, ...) bytes (split-K partials; may be 0).
  * Dequantisation of e4m3 codes is exact.  With the fp8 cache the latent QK and PV products
  * run on fp16 MFMA and the RoPE product on bf16 MFMA, all with fp32 accumulation: the bf16
  * latent query is rounded to fp16 (an element beyond the fp16 range raises
  * ML4_FAULT_RANGE), the softmax weights are rounded to fp16 after the running-max shift.
+ * With the bf16 cache QK and the RoPE product run on bf16 MFMA with the query as given and
+ * PV on fp16 MFMA (the latent values must lie within the fp16 range).
  */
 int ml4_sparse_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
                           int32_t q_dtype, int32_t n_heads, int32_t rope_dim,
