@@ -510,6 +510,49 @@ def quantise_latent_rows(c32: np.ndarray, rope_bf16_bits: Optional[np.ndarray]) 
     return out
 
 
+def encode_bf16(v: np.ndarray) -> np.ndarray:
+    """Finite binary32 values -> bfloat16 bits, round to nearest with ties to even on the
+    16 dropped bits of the IEEE binary32 pattern (a carry into the exponent is the correct
+    rounding up to the next binade)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    assert np.all(np.isfinite(np.asarray(v, dtype=np.float32)))
+    keep = u >> 16
+    rest = u & 0xFFFF
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & 1) == 1))
+    return (keep + up.astype(np.uint64)).astype(np.uint16)
+
+
+def pack_latent_rows_bf16(c32: np.ndarray, rope_bf16_bits: Optional[np.ndarray]) -> np.ndarray:
+    """Second layout, write side [blog, ROCm implementation details › "FP8 潜在缓存" (the
+    uncompressed 1,152-B row)]: [n][512] binary32 latents (+ [n][64] bf16 RoPE bits, or None)
+    -> [n][576] bf16 bits, latents rounded to nearest even, RoPE copied (left zero when None:
+    a NoPE write does not touch those values)."""
+    c32 = np.asarray(c32, dtype=np.float32)
+    out = np.zeros((c32.shape[0], KV_LORA + ROPE_DIM), dtype=np.uint16)
+    out[:, :KV_LORA] = encode_bf16(c32)
+    if rope_bf16_bits is not None:
+        out[:, KV_LORA:] = np.asarray(rope_bf16_bits, dtype=np.uint16)
+    return out
+
+
+def quantise_latent_rows_e4m3(c32: np.ndarray, rope32: Optional[np.ndarray], kv_scale: float
+                              ) -> np.ndarray:
+    """Second layout, write side [blog, ROCm implementation details › "FP8 潜在缓存" (all 576
+    dims in E4M3 with one per-tensor scale)]: code = E4M3(x / kv_scale) in binary32, rounded
+    to nearest even and clamped to +-448, for the 512 latents and (when given) the 64 RoPE
+    values; [n][576] codes, RoPE codes left zero when None."""
+    scale = np.float32(kv_scale)
+    def q(x):
+        v = (np.asarray(x, dtype=np.float32) / scale).astype(np.float32)   # binary32 division
+        return encode_e4m3(np.clip(v, -E4M3_MAX, E4M3_MAX).astype(np.float32))
+    c32 = np.asarray(c32, dtype=np.float32)
+    out = np.zeros((c32.shape[0], KV_LORA + ROPE_DIM), dtype=np.uint8)
+    out[:, :KV_LORA] = q(c32)
+    if rope32 is not None:
+        out[:, KV_LORA:] = q(rope32)
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # 7. Split-context merge  [blog, Long context › DCP]
 # --------------------------------------------------------------------------------------

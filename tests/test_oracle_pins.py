@@ -568,3 +568,45 @@ def test_plain_e4m3_rows_equal_fp8_ds_mla_rows_with_uniform_power_of_two_scales(
                          q_scale=qs, kv_scale=ks)
         b = O.sparse_mla(seqs, ds, "fp8", qbf[..., :512 + rope], rope, idx, ln, 0.05, 0.3)
         assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
+
+
+def test_bf16_encoder_matches_torch_round_to_nearest_even():
+    """Random binary32 values over many binades, exact bf16 values, and every tie pattern
+    (low half 0x8000 with even and odd kept halves): the bits equal torch's float32 ->
+    bfloat16 cast."""
+    g = np.random.default_rng(11)
+    x = (g.standard_normal(20000) * np.exp(g.uniform(-30, 30, 20000))).astype(np.float32)
+    base = g.integers(0, 0x7F7F, 4000, dtype=np.uint32) << 16
+    ties = np.concatenate([base | 0x8000, base | 0x7FFF, base | 0x8001]).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0, 3.0e38])]).astype(np.float32)
+    got = O.encode_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_second_layout_writers_round_trip_through_their_readers():
+    """bf16 rows read back as the bf16-rounded latents and the RoPE bits as given; plain-E4M3
+    rows equal torch's float8_e4m3fn cast of clamp(x / kv_scale) in binary32 and read back
+    within half an E4M3 step (saturated beyond 448 * kv_scale)."""
+    g = np.random.default_rng(12)
+    c = (g.standard_normal((8, 512)) * 3).astype(np.float32)
+    c[0, :4] = [1000.0, -1000.0, 0.0, -0.0]                  # saturating and signed zeros
+    rope = (g.standard_normal((8, 64))).astype(np.float32)
+    rope_bits = O.encode_bf16(rope)
+    rows16 = O.pack_latent_rows_bf16(c, rope_bits)
+    cc, kr = O.latent_rows_bf16(rows16.reshape(1, 8, 576), np.arange(8), 64)
+    assert np.array_equal(cc, torch.from_numpy(c).to(torch.bfloat16).double().numpy())
+    assert np.array_equal(kr, O.decode_bf16(rope_bits))
+    kv_scale = 4.5 / 448
+    rows8 = O.quantise_latent_rows_e4m3(c, O.decode_bf16(rope_bits), kv_scale)
+    s32 = np.float32(kv_scale)
+    ref_c = torch.from_numpy(np.clip(c / s32, -448, 448).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(rows8[:, :512], ref_c)
+    cc8, kr8 = O.latent_rows_e4m3(rows8.reshape(1, 8, 576), np.arange(8), 64, kv_scale)
+    inside = np.abs(c) <= 448 * kv_scale
+    bound = np.maximum(np.abs(c) * 2.0 ** -4, 2.0 ** -10 * kv_scale) * (1 + 1e-6)
+    assert np.all(np.abs(cc8 - c)[inside] <= bound[inside])
+    assert np.all(np.abs(cc8[~inside]) == 448 * kv_scale)
+    assert np.all(np.abs(kr8 - O.decode_bf16(rope_bits)) <= np.maximum(
+        np.abs(O.decode_bf16(rope_bits)) * 2.0 ** -4, 2.0 ** -10 * kv_scale) * (1 + 1e-6))
