@@ -36,7 +36,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 
-#define ML4_ABI_VERSION 3
+#define ML4_ABI_VERSION 4
 
 enum ml4_status {
   ML4_OK = 0,
@@ -274,9 +274,12 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
  *   Quantiser, per scale group (the whole 128-dim key; each 128 latent values):
  *     scale = amax / 448,  code = E4M3(x / scale) rounded to nearest even and clamped to
  *     +-448, in binary32; an all-zero group stores scale 0 and zero codes.
- *   cache        ML4_IDX_FP8_132 (index) or ML4_LAT_FP8_656 (latent); rows are addressed
- *                as pool + slot * row_bytes with 0 <= slot < num_blocks * block_size and
- *                written through cache->pool (which these two entries treat as writable).
+ *   cache        ML4_IDX_FP8_132 (index), ML4_LAT_FP8_656 or ML4_LAT_BF16_1152 (latent; the
+ *                bf16 row takes the latents rounded to nearest even and the RoPE bits as
+ *                given); rows are addressed as pool + slot * row_bytes with
+ *                0 <= slot < num_blocks * block_size and written through cache->pool (which
+ *                the write entries treat as writable).  ML4_LAT_E4M3_576 goes through
+ *                ml4_latent_cache_write_e4m3.
  *   block_size   tokens per block (power of two, 16 .. 65536).
  *   k / c        [n_tokens][128] / [n_tokens][512], BF16 or F32 (src_dtype).
  *   k_rope       [n_tokens][64] bf16 with rope_dim 64; NULL with rope_dim 0 (NoPE: the RoPE
@@ -294,6 +297,26 @@ int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const
                            int32_t src_dtype, const void* k_rope, int32_t rope_dim,
                            int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
                            hipStream_t stream);
+
+/*
+ * ml4_latent_cache_write_e4m3 -- ml4_latent_cache_write into plain E4M3 rows with one
+ * per-tensor scale (the second latent layout read by ml4_sparse_mla_decode_e4m3).
+ * [blog, ROCm implementation details › FP8 潜在缓存 (all 576 dims in E4M3 with a per-tensor
+ * scale, 576 B per token)]
+ *   Row: 512 latent codes then 64 RoPE codes, code = E4M3(x / kv_scale) rounded to nearest
+ *   even and clamped to +-448, in binary32; values beyond 448 * kv_scale saturate.
+ *   cache        ML4_LAT_E4M3_576.
+ *   kv_scale     the per-tensor scale the reader multiplies by; finite and > 0, else
+ *                ML4_E_INVALID.
+ *   k_rope       [n_tokens][64] bf16 with rope_dim 64 (quantised with kv_scale); NULL with
+ *                rope_dim 0 (the RoPE codes of the row are left untouched).
+ *   Other arguments, errors and device faults as ml4_latent_cache_write; a non-finite
+ *   latent or RoPE value sets ML4_FAULT_RANGE (that row is unspecified).
+ */
+int ml4_latent_cache_write_e4m3(const ml4_cache* lat_cache, int32_t block_size, const void* c,
+                                int32_t src_dtype, const void* k_rope, int32_t rope_dim,
+                                float kv_scale, int64_t n_tokens, const int64_t* slot_mapping,
+                                uint32_t* fault, hipStream_t stream);
 
 /*
  * ml4_topk_merge -- exact top-k over the union of per-shard candidate lists, for context

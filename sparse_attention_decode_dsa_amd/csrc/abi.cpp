@@ -473,10 +473,11 @@ int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache
 
 namespace {
 
-int cache_write(const char* entry, bool latent, const ml4_cache* cache, int32_t block_size,
-                const void* src, int32_t src_dtype, const void* rope, int32_t rope_dim,
-                int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
-                hipStream_t stream) {
+// e4m3: the ml4_latent_cache_write_e4m3 entry (kv_scale used); else kv_scale is ignored.
+int cache_write(const char* entry, bool latent, bool e4m3, const ml4_cache* cache,
+                int32_t block_size, const void* src, int32_t src_dtype, const void* rope,
+                int32_t rope_dim, float kv_scale, int64_t n_tokens,
+                const int64_t* slot_mapping, uint32_t* fault, hipStream_t stream) {
   Checks c;
   if (!cache) {
     c.bad(true, latent ? "lat_cache is NULL" : "idx_cache is NULL");
@@ -484,9 +485,15 @@ int cache_write(const char* entry, bool latent, const ml4_cache* cache, int32_t 
     c.bad(!cache->pool, "cache.pool is NULL");
     c.bad(!aligned(cache->pool, 16), "cache.pool must be 16-byte aligned");
     c.bad(cache->num_blocks < 1, "cache.num_blocks must be >= 1");
-    if (latent)
-      c.unsup(cache->format != ML4_LAT_FP8_656, "cache.format must be ML4_LAT_FP8_656");
-    else
+    if (e4m3) {
+      c.unsup(cache->format != ML4_LAT_E4M3_576, "cache.format must be ML4_LAT_E4M3_576");
+    } else if (latent) {
+      c.unsup(cache->format == ML4_LAT_E4M3_576,
+              "an ML4_LAT_E4M3_576 cache takes a scale: use ml4_latent_cache_write_e4m3");
+      c.unsup(cache->format != ML4_LAT_FP8_656 && cache->format != ML4_LAT_BF16_1152 &&
+                  cache->format != ML4_LAT_E4M3_576,
+              "cache.format must be ML4_LAT_FP8_656 or ML4_LAT_BF16_1152");
+    } else
       c.unsup(cache->format != ML4_IDX_FP8_132, "cache.format must be ML4_IDX_FP8_132");
   }
   c.bad(!pow2(block_size), "block_size must be a power of two");
@@ -505,10 +512,15 @@ int cache_write(const char* entry, bool latent, const ml4_cache* cache, int32_t 
     c.bad(rope_dim && n_tokens > 0 && (!rope || !aligned(rope, 8)),
           "k_rope must be non-NULL and 8-byte aligned when rope_dim is 64");
   }
+  if (e4m3)
+    c.bad(!(std::isfinite(kv_scale) && kv_scale > 0.f), "kv_scale must be finite and > 0");
   c.unsup(n_tokens > ((int64_t)1 << 31), "n_tokens above 2^31");
   if (int rc = c.finish(entry)) return rc;
   ml4::CacheWriteLaunch a{};
   a.latent = latent;
+  a.bf16_rows = latent && cache->format == ML4_LAT_BF16_1152;
+  a.e4m3_rows = e4m3;
+  a.kv_scale = kv_scale;
   a.pool = const_cast<void*>(cache->pool);   // the write entries own the rows they write
   a.capacity = cache->num_blocks * (int64_t)block_size;
   a.src = src;
@@ -526,16 +538,25 @@ int cache_write(const char* entry, bool latent, const ml4_cache* cache, int32_t 
 int ml4_index_cache_write(const ml4_cache* idx_cache, int32_t block_size, const void* k,
                           int32_t src_dtype, int64_t n_tokens, const int64_t* slot_mapping,
                           uint32_t* fault, hipStream_t stream) {
-  return cache_write("ml4_index_cache_write", false, idx_cache, block_size, k, src_dtype,
-                     nullptr, 0, n_tokens, slot_mapping, fault, stream);
+  return cache_write("ml4_index_cache_write", false, false, idx_cache, block_size, k,
+                     src_dtype, nullptr, 0, 0.f, n_tokens, slot_mapping, fault, stream);
 }
 
 int ml4_latent_cache_write(const ml4_cache* lat_cache, int32_t block_size, const void* c,
                            int32_t src_dtype, const void* k_rope, int32_t rope_dim,
                            int64_t n_tokens, const int64_t* slot_mapping, uint32_t* fault,
                            hipStream_t stream) {
-  return cache_write("ml4_latent_cache_write", true, lat_cache, block_size, c, src_dtype,
-                     k_rope, rope_dim, n_tokens, slot_mapping, fault, stream);
+  return cache_write("ml4_latent_cache_write", true, false, lat_cache, block_size, c,
+                     src_dtype, k_rope, rope_dim, 0.f, n_tokens, slot_mapping, fault, stream);
+}
+
+int ml4_latent_cache_write_e4m3(const ml4_cache* lat_cache, int32_t block_size, const void* c,
+                                int32_t src_dtype, const void* k_rope, int32_t rope_dim,
+                                float kv_scale, int64_t n_tokens, const int64_t* slot_mapping,
+                                uint32_t* fault, hipStream_t stream) {
+  return cache_write("ml4_latent_cache_write_e4m3", true, true, lat_cache, block_size, c,
+                     src_dtype, k_rope, rope_dim, kv_scale, n_tokens, slot_mapping, fault,
+                     stream);
 }
 
 int ml4_topk_merge(int32_t rows, int32_t n_shards, const float* cand_scores,

@@ -1,5 +1,6 @@
 // KV-cache writes on gfx950: quantise and pack new tokens into the 132-byte indexer rows and
-// the 656-byte fp8_ds_mla latent rows read by the rest of the path.
+// the latent rows read by the rest of the path (656-byte fp8_ds_mla, and the two second
+// layouts: 1,152-byte bf16 and 576-byte plain E4M3 with one per-tensor scale).
 //
 // Pages: "vLLM 首日支持 Mistral Large 4" (best2ai.com), ROCm implementation details ›
 // AITER 上的 DSA 索引器 (an FP8 indexer key with a single scale per key, 132 bytes per token)
@@ -13,6 +14,12 @@
 // a 128-value group reduce their maximum with xor shuffles, and lanes 0..15 copy the RoPE
 // bytes.  Both are streams: 256 B (bf16 key) or 1,160 B (bf16 latent + RoPE) read and 132 or
 // 656 B written per token.
+//
+// Second layouts [same page, › FP8 潜在缓存: the uncompressed bf16 row and the per-tensor-scale
+// E4M3 row]: the bf16 row takes the latents rounded to nearest even and the RoPE bits as
+// given; the E4M3 row takes code = E4M3(x / kv_scale), clamped to +-448 and rounded to
+// nearest even in binary32, for the latents and the RoPE values alike.  Same one wave per
+// token, eight latents per lane, lanes 0..15 on the RoPE values.
 #include "ml4_device.h"
 
 namespace ml4 {
@@ -21,6 +28,8 @@ namespace {
 
 constexpr int kIdxRowBytes = 132;
 constexpr int kLatRowBytes = 656;
+constexpr int kBf16RowBytes = 1152;
+constexpr int kE4m3RowBytes = 576;
 constexpr int kWavesPerWg = 4;
 constexpr float kE4m3Max = 448.0f;
 constexpr uint32_t kFaultSlot = 1u << 0;
@@ -34,6 +43,11 @@ __device__ __forceinline__ float load_value(const void* p, bool bf16, size_t i) 
 // the low 16 bits.
 __device__ __forceinline__ uint32_t to_e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 __device__ __forceinline__ float quantise_input(float x, float scale) {
@@ -108,12 +122,81 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write(CacheWrite
   }
 }
 
+__global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_bf16(CacheWriteLaunch a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;
+  const int64_t slot = dest_slot(a, token);
+  if (slot < 0) return;
+  uint32_t w[4];
+  bool finite = true;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = load_value(a.src, a.bf16, token * 512 + 8 * lane + 2 * e);
+    const float x1 = load_value(a.src, a.bf16, token * 512 + 8 * lane + 2 * e + 1);
+    finite &= __builtin_isfinite(x0) && __builtin_isfinite(x1);
+    w[e] = bf16_bits(x0) | (bf16_bits(x1) << 16);
+  }
+  if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
+  uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kBf16RowBytes;
+  *reinterpret_cast<u32x4*>(row + 16 * lane) = u32x4{w[0], w[1], w[2], w[3]};
+  if (a.rope_dim && lane < 16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.rope) +
+                                                     (size_t)token * 128 + 8 * lane);
+    *reinterpret_cast<uint2*>(row + 1024 + 8 * lane) = v;
+  }
+}
+
+__global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_e4m3(CacheWriteLaunch a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;
+  const int64_t slot = dest_slot(a, token);
+  if (slot < 0) return;
+  const float scale = a.kv_scale;
+  float x[8];
+  bool finite = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = load_value(a.src, a.bf16, token * 512 + 8 * lane + e);
+    finite &= __builtin_isfinite(x[e]);
+  }
+  float r[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool has_rope = a.rope_dim && lane < 16;
+  if (has_rope) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (float)static_cast<const __bf16*>(a.rope)[(size_t)token * 64 + 4 * lane + e];
+      finite &= __builtin_isfinite(r[e]);
+    }
+  }
+  if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = to_e4m3x2(quantise_input(x[4 * h], scale), quantise_input(x[4 * h + 1], scale));
+    const uint32_t hi = to_e4m3x2(quantise_input(x[4 * h + 2], scale), quantise_input(x[4 * h + 3], scale));
+    w[h] = lo | (hi << 16);
+  }
+  uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kE4m3RowBytes;
+  *reinterpret_cast<u32x2*>(row + 8 * lane) = u32x2{w[0], w[1]};
+  if (has_rope) {
+    const uint32_t lo = to_e4m3x2(quantise_input(r[0], scale), quantise_input(r[1], scale));
+    const uint32_t hi = to_e4m3x2(quantise_input(r[2], scale), quantise_input(r[3], scale));
+    *reinterpret_cast<uint32_t*>(row + 512 + 4 * lane) = lo | (hi << 16);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_cache_write(const CacheWriteLaunch& a, hipStream_t st) {
   if (a.n_tokens == 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_tokens + kWavesPerWg - 1) / kWavesPerWg));
-  if (a.latent)
+  if (a.latent && a.bf16_rows)
+    k_latent_write_bf16<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
+  else if (a.latent && a.e4m3_rows)
+    k_latent_write_e4m3<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
+  else if (a.latent)
     k_latent_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
   else
     k_index_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);

@@ -74,7 +74,10 @@ size_t mla_ws_bytes(const SeqView& s, int n_heads, int top_k);
 hipError_t launch_mla(const MlaLaunch& a, hipStream_t st);
 
 struct CacheWriteLaunch {
-  bool latent;          // 656-B fp8_ds_mla rows; else 132-B indexer rows
+  bool latent;          // latent rows (656-B fp8_ds_mla unless a flag below); else 132-B indexer rows
+  bool bf16_rows;       // latent: 1,152-B bf16 rows
+  bool e4m3_rows;       // latent: 576-B plain E4M3 rows, codes = E4M3(x / kv_scale)
+  float kv_scale;       // e4m3_rows: per-tensor scale, finite and > 0
   void* pool;
   int64_t capacity;     // num_blocks * block_size rows
   const void* src;      // [n_tokens][128 | 512]

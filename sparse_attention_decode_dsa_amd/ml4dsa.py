@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ML4DSA_LIB") or os.path.join(PKG, "libml4dsa.so")
 
 # ---- constants mirrored from include/ml4dsa.h
-ML4_ABI_VERSION = 3
+ML4_ABI_VERSION = 4
 ML4_OK, ML4_E_INVALID, ML4_E_UNSUPPORTED, ML4_E_WORKSPACE, ML4_E_LAUNCH, ML4_E_DEVICE_FAULT = (
     0, -1, -2, -3, -4, -5)
 ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
@@ -27,7 +27,8 @@ ML4_FAULT_RANGE = 16
 ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
-           "ml4_sparse_mla_decode_e4m3", "ml4_sparse_attn_layer", "ml4_window_mla_decode", "ml4_index_cache_write", "ml4_latent_cache_write",
+           "ml4_sparse_mla_decode_e4m3", "ml4_sparse_attn_layer", "ml4_window_mla_decode",
+           "ml4_index_cache_write", "ml4_latent_cache_write", "ml4_latent_cache_write_e4m3",
            "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
            "ml4_fault_query", "ml4_abi_version")
 
@@ -97,6 +98,9 @@ def _load() -> C.CDLL:
     lib.ml4_latent_cache_write.restype = C.c_int
     lib.ml4_latent_cache_write.argtypes = [P(ml4_cache), i32, vp, i32, vp, i32, i64, vp, vp,
                                            vp]
+    lib.ml4_latent_cache_write_e4m3.restype = C.c_int
+    lib.ml4_latent_cache_write_e4m3.argtypes = [P(ml4_cache), i32, vp, i32, vp, i32, f32, i64,
+                                                vp, vp, vp]
     lib.ml4_window_mla_decode.restype = C.c_int
     lib.ml4_window_mla_decode.argtypes = [P(ml4_seqs), P(ml4_cache), vp, i32, i32, i32, i32,
                                           f32, f32, vp, i32, vp, vp, sz, vp, vp]
@@ -250,6 +254,15 @@ def ml4_latent_cache_write(lat_cache, block_size, c, src_dtype, k_rope, rope_dim
     rc = LIB.ml4_latent_cache_write(C.byref(lat_cache), block_size, ptr(c), src_dtype,
                                     ptr(k_rope), rope_dim, n_tokens, ptr(slot_mapping),
                                     ptr(fault), stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_latent_cache_write_e4m3(lat_cache, block_size, c, src_dtype, k_rope, rope_dim, kv_scale,
+                                n_tokens, slot_mapping, fault=None, stream=None,
+                                check=True) -> int:
+    rc = LIB.ml4_latent_cache_write_e4m3(C.byref(lat_cache), block_size, ptr(c), src_dtype,
+                                         ptr(k_rope), rope_dim, float(kv_scale), n_tokens,
+                                         ptr(slot_mapping), ptr(fault), stream_handle(stream))
     return _check(rc) if check else rc
 
 

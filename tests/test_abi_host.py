@@ -179,3 +179,31 @@ def test_cache_write_default_deny_lists_every_reason():
     rc = M.ml4_latent_cache_write(c2, 64, None, M.ML4_BF16, None, 64, 0, None, None, stream=0,
                                   check=False)
     assert rc == M.ML4_OK
+
+
+def test_second_layout_cache_writes_default_deny():
+    """The plain-E4M3 latent cache is written only through the entry that takes its scale;
+    that entry refuses any other format and a scale that is not finite and positive; the
+    bf16 cache goes through the generic entry."""
+    c = M.ml4_cache()
+    c.pool, c.num_blocks, c.format = 4096, 4, M.ML4_LAT_E4M3_576
+    rc = M.ml4_latent_cache_write(c, 64, None, M.ML4_BF16, None, 0, 0, None, None, stream=0,
+                                  check=False)
+    assert rc == M.ML4_E_UNSUPPORTED and "ml4_latent_cache_write_e4m3" in M.ml4_last_error()
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        rc = M.ml4_latent_cache_write_e4m3(c, 64, None, M.ML4_BF16, None, 0, bad, 0, None,
+                                           None, stream=0, check=False)
+        assert rc == M.ML4_E_INVALID and "kv_scale" in M.ml4_last_error(), bad
+    assert M.ml4_latent_cache_write_e4m3(c, 64, None, M.ML4_BF16, None, 64, 0.5, 0, None,
+                                         None, stream=0, check=False) == M.ML4_OK
+    c.format = M.ML4_LAT_FP8_656
+    rc = M.ml4_latent_cache_write_e4m3(c, 64, None, M.ML4_BF16, None, 0, 0.5, 0, None, None,
+                                       stream=0, check=False)
+    assert rc == M.ML4_E_UNSUPPORTED and "ML4_LAT_E4M3_576" in M.ml4_last_error()
+    c.format = M.ML4_LAT_BF16_1152
+    assert M.ml4_latent_cache_write(c, 64, None, M.ML4_F32, None, 64, 0, None, None,
+                                    stream=0, check=False) == M.ML4_OK
+    c.format = M.ML4_LAT_F32
+    rc = M.ml4_latent_cache_write(c, 64, None, M.ML4_F32, None, 64, 0, None, None, stream=0,
+                                  check=False)
+    assert rc == M.ML4_E_UNSUPPORTED
