@@ -225,8 +225,9 @@ def time_layouts(case, run, dev: str, reps: int = 10):
 
 
 def time_cache_writes(n: int, dev: str, reps: int = 10):
-    """Quantise-and-pack of n new bf16 tokens into both caches (scattered slots).  Bytes per
-    token: index 128 x 2 in + 8 slot + 132 out; latent 512 x 2 + 64 x 2 in + 8 + 656 out."""
+    """Quantise-and-pack of n new bf16 tokens into the caches (scattered slots).  Bytes per
+    token: index 128 x 2 in + 8 slot + 132 out; latent 512 x 2 + 64 x 2 in + 8 + 656 out;
+    second layouts the same reads + 1,152 (bf16 rows) or 576 (plain E4M3 rows) out."""
     import torch
 
     from sparse_attention_decode_dsa_amd import ml4dsa as M
@@ -239,13 +240,20 @@ def time_cache_writes(n: int, dev: str, reps: int = 10):
     slots = torch.randperm(nb * bs, device=dev, generator=g)[:n].to(torch.int64)
     ipool = torch.empty((nb, bs, 132), dtype=torch.uint8, device=dev)
     lpool = torch.empty((nb, bs, 656), dtype=torch.uint8, device=dev)
+    bpool = torch.empty((nb, bs, 1152), dtype=torch.uint8, device=dev)
+    epool = torch.empty((nb, bs, 576), dtype=torch.uint8, device=dev)
     fault = torch.zeros(1, dtype=torch.int32, device=dev)
     ic, lc = M.make_cache(ipool, M.ML4_IDX_FP8_132), M.make_cache(lpool, M.ML4_LAT_FP8_656)
+    bc, ec = M.make_cache(bpool, M.ML4_LAT_BF16_1152), M.make_cache(epool, M.ML4_LAT_E4M3_576)
     out = {"tokens": n}
     for name, fn, per_tok in (
             ("index", lambda: M.ml4_index_cache_write(ic, bs, k, M.ML4_BF16, n, slots, fault), 396),
             ("latent", lambda: M.ml4_latent_cache_write(lc, bs, c, M.ML4_BF16, kr, 64, n, slots,
-                                                        fault), 1816)):
+                                                        fault), 1816),
+            ("latent_bf16_rows", lambda: M.ml4_latent_cache_write(
+                bc, bs, c, M.ML4_BF16, kr, 64, n, slots, fault), 2312),
+            ("latent_e4m3_rows", lambda: M.ml4_latent_cache_write_e4m3(
+                ec, bs, c, M.ML4_BF16, kr, 64, 0.01, n, slots, fault), 1736)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -16,9 +16,11 @@
 // which moves keys across the top-k boundary.)
 //
 // A work-group owns one request's run of up to 4 query rows and a chunk of its keys.  Key
-// rows stream from HBM in 64-key steps (8,448 contiguous bytes when a block holds >= 64
-// tokens): each thread loads 32 bytes of a row, decodes them to fp16 and writes them to a
-// double-buffered LDS tile, so a key is fetched and decoded once for all rows.  Each wave
+// rows stream from HBM in steps of 64 keys (4 rows per work-group) or 128 keys (1 or 2
+// rows: half as many barriers per key, measured 9 % faster for 2-row verify and 1 % for
+// decode, while 4 rows lose 5 % to register pressure): each thread loads 32 bytes of a row
+// (of two rows, 64 keys apart, in 128-key steps), decodes them to fp16 and writes them to
+// a double-buffered LDS tile, so a key is fetched and decoded once for all rows.  Each wave
 // owns one query row (its 64 x 128 query stays in registers) and 16-key sub-tiles of the
 // step; the weighted-ReLU head reduction runs in-lane over the 4 heads a lane holds per
 // tile, then across the 4 lane groups.
@@ -29,7 +31,9 @@ namespace ml4 {
 namespace {
 
 constexpr int kIdxRow = 132;
-constexpr int kStepKeys = 64;
+// Keys per staging step for R query rows per work-group.
+template <int R>
+constexpr int step_keys() { return R == 4 ? 64 : 128; }
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kKeyStride = 136;   // fp16 per key row in LDS (128 + 8): conflict-free b128 reads
@@ -52,8 +56,10 @@ constexpr int kMaxKeysPerWg = 4096;
 
 // R = query rows per work-group (1, 2 or 4), HT = 16-head tiles (n_heads / 16).
 template <int R, int HT>
-__global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int groups_per_seq,
-                                                          int keys_per_wg) {
+__global__ __launch_bounds__(kThreads)
+void k_indexer_fp8(IndexerLaunch a, int groups_per_seq, int keys_per_wg) {
+  constexpr int kStepKeys = step_keys<R>();
+  constexpr int kHalves = kStepKeys / 64;        // staged keys per thread and step
   __shared__ __attribute__((aligned(16))) _Float16 ktile[2][kStepKeys * kKeyStride];
   __shared__ float kscale[2][kStepKeys];
   __shared__ int kok[2][kStepKeys / 16];
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
     pos = -1;
   }
   // The 4/R waves of a row split the step's four 16-key sub-tiles: wave / R, + 4 / R, ...
-  constexpr int kSubPerWave = R;
+  constexpr int kSubPerWave = (kStepKeys / 16) * R / kWaves;
   const int sub0 = wave / R;
 
   const int32_t* bt = s.block_table + (size_t)b * s.mbps;
@@ -146,20 +152,22 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
   if (nsteps <= 0) return;
   __syncthreads();   // blk_sh
 
-  // Staging: thread -> (key kk = tid / 4, quarter qq = tid % 4) of a 64-key step.  Two
-  // register sets keep the loads of two steps in flight.
+  // Staging: thread -> (keys kk + 64 j, quarter qq = tid % 4) of a step, kk = tid / 4.
+  // Two register sets keep the loads of two steps in flight.
   const int kk = tid >> 2, qq = tid & 3;
-  struct Stage {
+  struct Half {
     u32x4 lo, hi;
     float scale;
     int ok;
   };
-  auto load_step = [&](Stage& S, int t0) {
+  struct Stage {
+    Half h[kHalves];
+  };
+  auto load_half = [&](Half& S, int t) {
     S.lo = u32x4{0, 0, 0, 0};
     S.hi = u32x4{0, 0, 0, 0};
     S.scale = 0.f;
     S.ok = 0;
-    const int t = t0 + kk;
     if (t >= k_end) return;      // past every row: nothing is read
     const int blk = blk_sh[(t - k_lo) >> 4];
     if (blk < 0) return;
@@ -171,8 +179,12 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
     if (qq == 0) S.scale = *reinterpret_cast<const float*>(rp + 128);
     S.ok = 1;
   };
-  auto store_step = [&](const Stage& S, int buf) {
-    _Float16* dst = &ktile[buf][kk * kKeyStride + 32 * qq];
+  auto load_step = [&](Stage& S, int t0) {
+#pragma unroll
+    for (int j = 0; j < kHalves; ++j) load_half(S.h[j], t0 + 64 * j + kk);
+  };
+  auto store_half = [&](const Half& S, int buf, int key) {
+    _Float16* dst = &ktile[buf][key * kKeyStride + 32 * qq];
     const uint32_t w8[8] = {S.lo[0], S.lo[1], S.lo[2], S.lo[3],
                             S.hi[0], S.hi[1], S.hi[2], S.hi[3]};
 #pragma unroll
@@ -182,17 +194,23 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
       *reinterpret_cast<f16x8*>(dst + 8 * c) =
           f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    if (qq == 0) kscale[buf][kk] = S.scale;
-    if (qq == 0 && (kk & 15) == 0) kok[buf][kk >> 4] = S.ok;
+    if (qq == 0) kscale[buf][key] = S.scale;
+    if (qq == 0 && (key & 15) == 0) kok[buf][key >> 4] = S.ok;
   };
-  // Scores of one 64-key step for this wave's row.  Each lane accumulates, per sub-tile, the
-  // weighted ReLU over the 4 heads of each head tile it holds; one cross-lane transpose-sum
-  // (two permlane32 and one permlane16 swap) then leaves sub-tile g's totals in lane group g,
-  // so the row's results leave in one store per step.  K fragments of the next sub-tile are
+  auto store_step = [&](const Stage& S, int buf) {
+#pragma unroll
+    for (int j = 0; j < kHalves; ++j) store_half(S.h[j], buf, 64 * j + kk);
+  };
+  // Scores of one step for this wave's row.  Each lane accumulates, per sub-tile, the
+  // weighted ReLU over the 4 heads of each head tile it holds; a cross-lane transpose-sum
+  // (two permlane32 and one permlane16 swap) per four sub-tiles then leaves sub-tile g's
+  // totals in lane group g, so the row's results leave in one store per four sub-tiles.  K fragments of the next sub-tile are
   // read while the current one multiplies.
   auto compute_step = [&](int st, int buf) {
     const int t0 = k_lo + st * kStepKeys;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part[kSubPerWave];
+#pragma unroll
+    for (int i = 0; i < kSubPerWave; ++i) part[i] = 0.f;
     f16x8 kb[2][4];
     auto read_frags = [&](f16x8 (&dst)[4], int sub) {
       const _Float16* krow = &ktile[buf][(16 * sub + c16) * kKeyStride + 32 * g16];
@@ -212,12 +230,19 @@ __global__ __launch_bounds__(kThreads) void k_indexer_fp8(IndexerLaunch a, int g
         for (int i = 0; i < 4; ++i) part[si] = fmaf(wq[ht][i], relu_bits(d[i]), part[si]);
       }
     }
-    const float tot = sum_over_lane_groups(part);
-    const int sub = sub0 + g16 * (kWaves / R);     // this lane group's sub-tile
-    const int t = t0 + 16 * sub + c16;
-    if (row_live && g16 < kSubPerWave && t < k_hi) {
-      const bool ok = t < k_end && t <= pos && kok[buf][sub] != 0;
-      a.scores[(size_t)row * a.ld + t] = ok ? tot * kscale[buf][16 * sub + c16] * mrow : ninf;
+#pragma unroll
+    for (int h = 0; h < (kSubPerWave + 3) / 4; ++h) {
+      float p4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p4[j] = 4 * h + j < kSubPerWave ? part[4 * h + j] : 0.f;
+      const float tot = sum_over_lane_groups(p4);
+      const int sl = 4 * h + g16;                    // this lane group's sub-tile of the wave
+      const int sub = sub0 + sl * (kWaves / R);
+      const int t = t0 + 16 * sub + c16;
+      if (row_live && sl < kSubPerWave && t < k_hi) {
+        const bool ok = t < k_end && t <= pos && kok[buf][sub] != 0;
+        a.scores[(size_t)row * a.ld + t] = ok ? tot * kscale[buf][16 * sub + c16] * mrow : ninf;
+      }
     }
   };
 
