@@ -17,8 +17,9 @@
 //
 // A work-group owns one request's run of up to 4 query rows and a chunk of its keys.  Key
 // rows stream from HBM in steps of 64 keys (4 rows per work-group) or 128 keys (1 or 2
-// rows: half as many barriers per key, measured 9 % faster for 2-row verify and 1 % for
-// decode, while 4 rows lose 5 % to register pressure): each thread loads 32 bytes of a row
+// rows: half as many barriers per key, measured 9 % faster for a 1M-key single-row decode,
+// 3 % for 2-row verify and 1 % for 8 x 32k decode, while 4 rows lose 5 % to register
+// pressure): each thread loads 32 bytes of a row
 // (of two rows, 64 keys apart, in 128-key steps), decodes them to fp16 and writes them to
 // a double-buffered LDS tile, so a key is fetched and decoded once for all rows.  Each wave
 // owns one query row (its 64 x 128 query stays in registers) and 16-key sub-tiles of the
