@@ -185,6 +185,43 @@ def test_topk_exact_on_given_scores(n, top_k, seed):
         assert np.array_equal(gi[r], oi), f"row {r}: first diff at {np.argmax(gi[r] != oi)}"
 
 
+def test_topk_long_rows_of_mixed_lengths():
+    """The multi-work-group selection (rows above 131,072 positions) with rows of unequal
+    length in one launch: a row shorter than k (returned whole), one in the one-work-group
+    range and long rows whose chunk counts differ, so some work-groups of the grid have no
+    keys of their row; every row equals the oracle's, and a second call on the same
+    workspace gives the same result."""
+    lens = [140000, 1500, 200003, 70000, 131073]
+    top_k = 2048
+    _say(f"[gpu] topk mixed long rows {lens} k={top_k}")
+    n_max = max(lens)
+    ld = (n_max + 3) // 4 * 4
+    scores = torch.full((len(lens), ld), -5.0)
+    for i, n in enumerate(lens):
+        x = _rand_scores(n, 900 + i, dup_levels=[None, 4, 16, None, 2][i])
+        scores[i, :n] = x
+    batch = synth.make_batch(77, lens, [1] * len(lens), 64, device=DEV)
+    seqs = M.make_seqs(batch)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_TOPK, seqs, 0, top_k)
+    assert wsn > 0
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    sd = scores.to(DEV)
+    sn = scores.numpy().astype(np.float64)
+    pos = t_np(batch.q_pos)
+    for call in range(2):
+        idx = torch.full((len(lens), top_k), -9, dtype=torch.int32, device=DEV)
+        ln = torch.zeros(len(lens), dtype=torch.int32, device=DEV)
+        fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+        M.ml4_topk_select(seqs, sd, ld, top_k, idx, ln, ws, wsn, fault)
+        torch.cuda.synchronize()
+        assert M.ml4_fault_query(fault) == 0
+        gi, gl = t_np(idx), t_np(ln)
+        for r in range(len(lens)):
+            oi, on = O.topk_row(sn[r], int(pos[r]), top_k)
+            assert gl[r] == on, (call, r)
+            assert np.array_equal(gi[r], oi), f"call {call} row {r}: first diff at {np.argmax(gi[r] != oi)}"
+
+
 @pytest.mark.parametrize("n,top_k,kind", [(20000, 2048, "const"), (50000, 2048, "tie_block"),
                                           (9000, 2048, "const")])
 def test_topk_when_the_candidate_list_overflows(n, top_k, kind):
