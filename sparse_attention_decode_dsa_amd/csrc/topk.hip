@@ -16,8 +16,9 @@
 // Rows up to 131,072 positions first narrow the row to an LDS candidate list with a
 // threshold taken from a sample (one read of the row), and run steps 2-3 on that list; the
 // streaming form above is their fallback when the list misses.  Longer rows use a
-// multi-work-group version with the same steps, one launch per step, its histograms merged
-// with integer atomics.
+// multi-work-group version with the same steps, one launch per pass over the row, its
+// histograms merged with integer atomics; each work-group of a pass redoes the per-row
+// digit pick from the previous pass's histogram, so no launch is spent on it.
 #include "ml4_device.h"
 
 namespace ml4 {
@@ -544,6 +545,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
 // Per-row selection state of the multi-work-group path.  The rule being refined is
 // "keep key if key >> shift > P; keep it if key >> shift == P and it is among the first
 // `need` such keys in t order"; `resolved` stops refinement once a bucket is taken whole.
+// Slot 0 of a row holds the AND/OR accumulators; slot p + 1 the state S_p that pass p
+// used (written by the pass's first work-group, read by the next launch).  Every
+// work-group of a pass derives S_p itself from S_{p-1} and the histogram of pass p - 1, so
+// no launch is spent on the per-row step and no work-group waits for another.
 struct alignas(16) BigState {
   uint32_t and_v, or_v, nan, active;
   uint64_t P;
@@ -551,10 +556,14 @@ struct alignas(16) BigState {
   int resolved, pad0, pad1, pad2;
 };
 
+constexpr int kBigSlots = 5;      // accumulators, S_0 .. S_3
+constexpr int kBigPasses = 3;     // 3 x 11 digit bits >= 32
+constexpr int kHistBins = 1 << kMaxDigitBits;
+
 struct BigWs {
-  BigState* st;    // [rows]
-  uint32_t* hist;  // [rows][2048]
-  int* cnt;        // [rows][chunks][2]  gt, eq  -> exclusive offsets after the scan
+  BigState* st;    // [rows][kBigSlots]
+  uint32_t* hist;  // [rows][kBigPasses][2048], one histogram per pass
+  int* cnt;        // [rows][chunks][2]  keys above / equal to the final threshold
   int chunks;
 };
 
@@ -564,9 +573,9 @@ __device__ __forceinline__ BigWs big_ws(void* ws, int rows, int chunks) {
   BigWs w;
   char* p = static_cast<char*>(ws);
   w.st = reinterpret_cast<BigState*>(p);
-  p += round256((size_t)rows * sizeof(BigState));
+  p += round256((size_t)rows * kBigSlots * sizeof(BigState));
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += round256((size_t)rows * (1 << kMaxDigitBits) * 4);
+  p += round256((size_t)rows * kBigPasses * kHistBins * 4);
   w.cnt = reinterpret_cast<int*>(p);
   w.chunks = chunks;
   return w;
@@ -598,23 +607,63 @@ __device__ __forceinline__ void load_run16(const float* row, int lo, int hi, uin
   *any_nan = nan;
 }
 
+__device__ __forceinline__ bool refining(const BigState& s) {
+  return s.active && s.shift > 0 && !s.resolved;
+}
+
+// S_p from S_{p-1} and pass p-1's histogram g (a kBigThreads work-group, every thread calls
+// it): the digit of the need-th key, thread i taking the 8 digits nb-1-8i .. nb-8-8i in
+// descending order.  A finished state is returned as it is.
+__device__ BigState pick_digit(const BigState& s, const uint32_t* g, int* sh_scan, int* sh_sel) {
+  if (!refining(s)) return s;
+  const int wd = min(kMaxDigitBits, s.shift), nb = 1 << wd;
+  constexpr int kBpt = kHistBins / kBigThreads;
+  uint32_t c[kBpt];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kBpt; ++j) {
+    const int d = nb - 1 - (kBpt * (int)threadIdx.x + j);
+    c[j] = d >= 0 ? g[d] : 0u;
+    sum += (int)c[j];
+  }
+  int total;
+  int ex = block_exclusive_scan<kBigThreads>(sum, &total, sh_scan);
+#pragma unroll
+  for (int j = 0; j < kBpt; ++j) {
+    const int d = nb - 1 - (kBpt * (int)threadIdx.x + j);
+    if (d >= 0 && ex < s.need && s.need <= ex + (int)c[j]) {
+      sh_sel[0] = d; sh_sel[1] = ex; sh_sel[2] = (int)c[j];
+    }
+    ex += (int)c[j];
+  }
+  __syncthreads();
+  BigState o = s;
+  o.P = (s.P << wd) | (uint64_t)sh_sel[0];
+  o.need = s.need - sh_sel[1];
+  o.shift = s.shift - wd;
+  o.resolved = (sh_sel[2] == o.need) ? 1 : 0;
+  __syncthreads();   // sh_sel is reused by the caller
+  return o;
+}
+
 __global__ __launch_bounds__(kBigThreads) void k_tkb_init(TopkLaunch a, int chunks) {
   const int r = blockIdx.x;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  for (int i = threadIdx.x; i < (1 << kMaxDigitBits); i += kBigThreads)
-    w.hist[(size_t)r * (1 << kMaxDigitBits) + i] = 0u;
+  for (int i = threadIdx.x; i < kBigPasses * kHistBins; i += kBigThreads)
+    w.hist[(size_t)r * kBigPasses * kHistBins + i] = 0u;
   int n = 0;
   const bool active = row_prologue(a, r, &n);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < kBigSlots) {   // every slot: an inactive row is never written again
     BigState s{~0u, 0u, 0u, active ? 1u : 0u, 0ull, 0, 0, 0, 0, 0, 0};
-    w.st[r] = s;
+    w.st[(size_t)r * kBigSlots + threadIdx.x] = s;
   }
 }
 
 __global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chunks) {
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  if (!w.st[r].active) return;
+  BigState& acc = w.st[(size_t)r * kBigSlots];
+  if (!acc.active) return;
   const int n = a.s.q_pos[r] + 1;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
   if (lo >= hi) return;
@@ -643,30 +692,39 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chu
   __syncthreads();
   if (threadIdx.x == 0) {   // one set of atomics per work-group
     for (int i = 1; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
-    atomicAnd(&w.st[r].and_v, av);
-    atomicOr(&w.st[r].or_v, ov);
-    if (sh_nan) atomicOr(&w.st[r].nan, 1u);
+    atomicAnd(&acc.and_v, av);
+    atomicOr(&acc.or_v, ov);
+    if (sh_nan) atomicOr(&acc.nan, 1u);
   }
 }
 
-__global__ void k_tkb_setup(TopkLaunch a, int chunks) {
-  const int r = blockIdx.x;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  if (threadIdx.x != 0 || !w.st[r].active) return;
-  BigState& s = w.st[r];
-  if (s.nan) raise_fault(a.fault, kFaultNan);
-  const uint32_t diff = s.and_v ^ s.or_v;
-  s.shift = diff ? 32 - __builtin_clz(diff) : 0;
-  s.P = digit_prefix(s.and_v, s.shift);
-  s.need = a.top_k;
-}
-
-__global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chunks) {
-  __shared__ uint32_t hist[1 << kMaxDigitBits];
+// Pass p: S_p (from the AND/OR prefix for p = 0, else by pick_digit from pass p - 1), then
+// this chunk's keys under the prefix P counted into pass p's histogram.
+__global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chunks, int pass) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ int sh_scan[kBigThreads / kWave];
+  __shared__ int sh_sel[4];
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[r];
-  if (!s.active || s.shift == 0 || s.resolved) return;
+  BigState* slots = w.st + (size_t)r * kBigSlots;
+  uint32_t* hrow = w.hist + (size_t)r * kBigPasses * kHistBins;
+  BigState s;
+  if (pass == 0) {
+    s = slots[0];
+    if (!s.active) return;
+    const uint32_t diff = s.and_v ^ s.or_v;
+    s.shift = diff ? 32 - __builtin_clz(diff) : 0;
+    s.P = digit_prefix(s.and_v, s.shift);
+    s.need = a.top_k;
+    s.resolved = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && s.nan) raise_fault(a.fault, kFaultNan);
+  } else {
+    s = slots[pass];
+    if (!s.active) return;
+    s = pick_digit(s, hrow + (size_t)(pass - 1) * kHistBins, sh_scan, sh_sel);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) slots[pass + 1] = s;
+  if (!refining(s)) return;
   const int n = a.s.q_pos[r] + 1;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
   if (lo >= hi) return;
@@ -682,38 +740,24 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chun
     if (((valid >> e) & 1u) && digit_prefix(k[e], s.shift) == s.P)
       atomicAdd(&hist[(k[e] >> nsh) & (nb - 1)], 1u);
   __syncthreads();
-  uint32_t* g = w.hist + (size_t)r * (1 << kMaxDigitBits);
+  uint32_t* g = hrow + (size_t)pass * kHistBins;
   for (int i = threadIdx.x; i < nb; i += kBigThreads)
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_tkb_pick(TopkLaunch a, int chunks) {
-  __shared__ int sh_scan[kRowThreads / kWave];
-  __shared__ int sh_sel[4];
-  const int r = blockIdx.x;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[r];
-  if (!s.active || s.shift == 0 || s.resolved) return;
-  const int wd = min(kMaxDigitBits, s.shift), nb = 1 << wd;
-  uint32_t* g = w.hist + (size_t)r * (1 << kMaxDigitBits);
-  find_digit<kRowThreads>(g, nb, s.need, sh_sel, sh_scan);
-  const int d = sh_sel[0], above = sh_sel[1], cnt = sh_sel[2];
-  for (int i = threadIdx.x; i < nb; i += kRowThreads) g[i] = 0u;
-  if (threadIdx.x == 0) {
-    BigState& o = w.st[r];
-    o.P = (s.P << wd) | (uint64_t)d;
-    o.need = s.need - above;
-    o.shift = s.shift - wd;
-    o.resolved = (cnt == o.need) ? 1 : 0;
-  }
-}
-
+// S_3 from the last pass's histogram, then this chunk's keys above / equal to the threshold.
 __global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chunks) {
   __shared__ int sh_gt[kBigThreads / kWave], sh_eq[kBigThreads / kWave];
+  __shared__ int sh_scan[kBigThreads / kWave];
+  __shared__ int sh_sel[4];
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[r];
+  BigState* slots = w.st + (size_t)r * kBigSlots;
+  BigState s = slots[kBigPasses];
   if (!s.active) return;
+  s = pick_digit(s, w.hist + ((size_t)r * kBigPasses + kBigPasses - 1) * kHistBins, sh_scan,
+                 sh_sel);
+  if (blockIdx.x == 0 && threadIdx.x == 0) slots[kBigPasses + 1] = s;
   const int shift = s.shift;
   const uint64_t P = s.P;
   const int n = a.s.q_pos[r] + 1;
@@ -745,41 +789,31 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chu
   }
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_tkb_scan(TopkLaunch a, int chunks) {
-  __shared__ int sh_scan[kRowThreads / kWave];
-  const int r = blockIdx.x;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  if (!w.st[r].active) return;
-  int* c = w.cnt + (size_t)r * chunks * 2;
-  int carry_gt = 0, carry_eq = 0;
-  for (int base = 0; base < chunks; base += kRowThreads) {
-    const int i = base + threadIdx.x;
-    const int g = i < chunks ? c[2 * i] : 0;
-    const int e = i < chunks ? c[2 * i + 1] : 0;
-    int tg, te;
-    const int xg = block_exclusive_scan<kRowThreads>(g, &tg, sh_scan);
-    const int xe = block_exclusive_scan<kRowThreads>(e, &te, sh_scan);
-    if (i < chunks) { c[2 * i] = carry_gt + xg; c[2 * i + 1] = carry_eq + xe; }
-    carry_gt += tg;
-    carry_eq += te;
-  }
-  if (threadIdx.x == 0) a.len[r] = a.top_k;
-}
-
 __global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chunks) {
   __shared__ int sh_scan[kBigThreads / kWave];
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[r];
+  const BigState s = w.st[(size_t)r * kBigSlots + kBigPasses + 1];
   if (!s.active) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.len[r] = a.top_k;
   const int shift = s.shift;
   const uint64_t P = s.P;
   const int n = a.s.q_pos[r] + 1;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
   if (lo >= hi) return;
-  const int* c = w.cnt + ((size_t)r * chunks + blockIdx.x) * 2;
-  // Keys above the threshold that precede this chunk, plus the equal keys taken before it.
-  const int gt_before = c[0], eq_before = c[1];
+  // Keys above the threshold that precede this chunk, plus the equal keys taken before it:
+  // sums over the counts of the chunks before this one.
+  const int* c = w.cnt + (size_t)r * chunks * 2;
+  int g_sum = 0, e_sum = 0;
+  for (int i = threadIdx.x; i < (int)blockIdx.x; i += kBigThreads) {
+    g_sum += c[2 * i];
+    e_sum += c[2 * i + 1];
+  }
+  int tot;
+  (void)block_exclusive_scan<kBigThreads>(g_sum, &tot, sh_scan);
+  const int gt_before = tot;
+  (void)block_exclusive_scan<kBigThreads>(e_sum, &tot, sh_scan);
+  const int eq_before = tot;
   const int eq_taken_before = min(eq_before, s.need);
   int carry_eq = eq_before, carry_out = gt_before + eq_taken_before;
   const int K = a.top_k;
@@ -798,7 +832,6 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chu
       gt |= (h > P ? 1u : 0u) << e;
       eq |= (h == P ? 1u : 0u) << e;
     }
-  int tot;
   int eq_rank = carry_eq + block_exclusive_scan<kBigThreads>(__builtin_popcount(eq), &tot, sh_scan);
   uint32_t sel = gt;
 #pragma unroll
@@ -826,7 +859,8 @@ size_t topk_ws_bytes(const SeqView& s, int top_k) {
   (void)top_k;
   if (s.max_seq_len <= 4 * kCacheKeys) return 0;
   const size_t rows = (size_t)s.total_q;
-  return round256(rows * sizeof(BigState)) + round256(rows * (1 << kMaxDigitBits) * 4) +
+  return round256(rows * kBigSlots * sizeof(BigState)) +
+         round256(rows * kBigPasses * kHistBins * 4) +
          round256(rows * (size_t)big_chunks(s) * 2 * sizeof(int));
 }
 
@@ -840,13 +874,9 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   const dim3 grid(chunks, s.total_q);
   k_tkb_init<<<s.total_q, kBigThreads, 0, st>>>(a, chunks);
   k_tkb_andor<<<grid, kBigThreads, 0, st>>>(a, chunks);
-  k_tkb_setup<<<s.total_q, 64, 0, st>>>(a, chunks);
-  for (int pass = 0; pass < 3; ++pass) {
-    k_tkb_hist<<<grid, kBigThreads, 0, st>>>(a, chunks);
-    k_tkb_pick<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
-  }
+  for (int pass = 0; pass < kBigPasses; ++pass)
+    k_tkb_hist<<<grid, kBigThreads, 0, st>>>(a, chunks, pass);
   k_tkb_count<<<grid, kBigThreads, 0, st>>>(a, chunks);
-  k_tkb_scan<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
   k_tkb_write<<<grid, kBigThreads, 0, st>>>(a, chunks);
   return hipGetLastError();
 }
