@@ -96,12 +96,24 @@ __device__ void find_digit(const uint32_t* hist, int nb, int need, int* out, int
   __syncthreads();
 }
 
-__device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_out) {
+// Row r's case: 0 = a selection over n > k positions, 1 = a position outside its request,
+// 2 = n <= k (the row is returned whole).  *n_out = p + 1 when the position is valid.
+// Called by whole waves.
+__device__ __forceinline__ int row_kind(const TopkLaunch& a, int r, int* n_out) {
   const SeqView& s = a.s;
   const int b = request_of_wave(s.q_start, s.batch, r);
   const int p = s.q_pos[r];
+  if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len || (int64_t)p >= a.ld) return 1;
+  *n_out = p + 1;
+  return p + 1 <= a.top_k ? 2 : 0;
+}
+
+// row_kind, plus the output of a row that needs no selection; true for a selection row.
+__device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_out) {
+  int n = 0;
+  const int kind = row_kind(a, r, &n);
   int32_t* out = a.idx + (size_t)r * a.top_k;
-  if (p < 0 || p >= s.seq_lens[b] || p >= s.max_seq_len || (int64_t)p >= a.ld) {
+  if (kind == 1) {
     for (int i = threadIdx.x; i < a.top_k; i += blockDim.x) out[i] = -1;
     if (threadIdx.x == 0) {
       a.len[r] = 0;
@@ -109,8 +121,7 @@ __device__ __forceinline__ bool row_prologue(const TopkLaunch& a, int r, int* n_
     }
     return false;
   }
-  const int n = p + 1;
-  if (n <= a.top_k) {
+  if (kind == 2) {
     for (int i = threadIdx.x; i < a.top_k; i += blockDim.x) out[i] = i < n ? i : -1;
     if (threadIdx.x == 0) a.len[r] = n;
     return false;
@@ -545,8 +556,9 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
 // Per-row selection state of the multi-work-group path.  The rule being refined is
 // "keep key if key >> shift > P; keep it if key >> shift == P and it is among the first
 // `need` such keys in t order"; `resolved` stops refinement once a bucket is taken whole.
-// Slot 0 of a row holds the AND/OR accumulators; slot p + 1 the state S_p that pass p
-// used (written by the pass's first work-group, read by the next launch).  Every
+// Slot p of a row holds the state S_p that pass p used (written by the pass's first
+// work-group, read by the next launch); the AND/OR pass leaves one (AND, OR, NaN) triple
+// per chunk, which pass 0 reduces.  Every
 // work-group of a pass derives S_p itself from S_{p-1} and the histogram of pass p - 1, so
 // no launch is spent on the per-row step and no work-group waits for another.
 struct alignas(16) BigState {
@@ -556,7 +568,7 @@ struct alignas(16) BigState {
   int resolved, pad0, pad1, pad2;
 };
 
-constexpr int kBigSlots = 5;      // accumulators, S_0 .. S_3
+constexpr int kBigSlots = 4;      // S_0 .. S_3
 constexpr int kBigPasses = 3;     // 3 x 11 digit bits >= 32
 constexpr int kHistBins = 1 << kMaxDigitBits;
 
@@ -564,6 +576,7 @@ struct BigWs {
   BigState* st;    // [rows][kBigSlots]
   uint32_t* hist;  // [rows][kBigPasses][2048], one histogram per pass
   int* cnt;        // [rows][chunks][2]  keys above / equal to the final threshold
+  u32x4* ao;       // [rows][chunks]     AND, OR, NaN flag of the chunk's keys
   int chunks;
 };
 
@@ -577,6 +590,8 @@ __device__ __forceinline__ BigWs big_ws(void* ws, int rows, int chunks) {
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += round256((size_t)rows * kBigPasses * kHistBins * 4);
   w.cnt = reinterpret_cast<int*>(p);
+  p += round256((size_t)rows * chunks * 2 * sizeof(int));
+  w.ao = reinterpret_cast<u32x4*>(p);
   w.chunks = chunks;
   return w;
 }
@@ -646,33 +661,33 @@ __device__ BigState pick_digit(const BigState& s, const uint32_t* g, int* sh_sca
   return o;
 }
 
-__global__ __launch_bounds__(kBigThreads) void k_tkb_init(TopkLaunch a, int chunks) {
-  const int r = blockIdx.x;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  for (int i = threadIdx.x; i < kBigPasses * kHistBins; i += kBigThreads)
-    w.hist[(size_t)r * kBigPasses * kHistBins + i] = 0u;
-  int n = 0;
-  const bool active = row_prologue(a, r, &n);
-  if (threadIdx.x < kBigSlots) {   // every slot: an inactive row is never written again
-    BigState s{~0u, 0u, 0u, active ? 1u : 0u, 0ull, 0, 0, 0, 0, 0, 0};
-    w.st[(size_t)r * kBigSlots + threadIdx.x] = s;
-  }
-}
-
+// AND/OR of each chunk's keys (the leading bits common to the row are skipped by pass 0).
+// Work-group 0 of each row also writes the output of a row that needs no selection and
+// clears the row's per-pass histograms.
 __global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chunks) {
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  BigState& acc = w.st[(size_t)r * kBigSlots];
-  if (!acc.active) return;
-  const int n = a.s.q_pos[r] + 1;
+  int n = 0;
+  if (row_kind(a, r, &n) != 0) {
+    if (blockIdx.x == 0) {
+      row_prologue(a, r, &n);
+      if (threadIdx.x < kBigSlots) {
+        const BigState idle{~0u, 0u, 0u, 0u, 0ull, 0, 0, 0, 0, 0, 0};
+        w.st[(size_t)r * kBigSlots + threadIdx.x] = idle;
+      }
+    }
+    return;
+  }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < kBigPasses * kHistBins; i += kBigThreads)
+      w.hist[(size_t)r * kBigPasses * kHistBins + i] = 0u;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
-  if (lo >= hi) return;
   __shared__ uint32_t sh_and[kBigThreads / kWave], sh_or[kBigThreads / kWave];
   __shared__ int sh_nan;
   const float* row = a.scores + (size_t)r * a.ld;
-  uint32_t k[16], valid;
-  bool any_nan;
-  load_run16(row, lo, hi, k, &valid, &any_nan);
+  uint32_t k[16], valid = 0u;
+  bool any_nan = false;
+  if (lo < hi) load_run16(row, lo, hi, k, &valid, &any_nan);   // else the identity is left
   uint32_t av = ~0u, ov = 0u;
 #pragma unroll
   for (int e = 0; e < 16; ++e)
@@ -690,11 +705,9 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chu
   if (any_nan) sh_nan = 1;
   if ((threadIdx.x & (kWave - 1)) == 0) { sh_and[threadIdx.x >> 6] = av; sh_or[threadIdx.x >> 6] = ov; }
   __syncthreads();
-  if (threadIdx.x == 0) {   // one set of atomics per work-group
+  if (threadIdx.x == 0) {
     for (int i = 1; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
-    atomicAnd(&acc.and_v, av);
-    atomicOr(&acc.or_v, ov);
-    if (sh_nan) atomicOr(&acc.nan, 1u);
+    w.ao[(size_t)r * chunks + blockIdx.x] = u32x4{av, ov, sh_nan ? 1u : 0u, 0u};
   }
 }
 
@@ -710,8 +723,30 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chun
   uint32_t* hrow = w.hist + (size_t)r * kBigPasses * kHistBins;
   BigState s;
   if (pass == 0) {
-    s = slots[0];
-    if (!s.active) return;
+    int n0 = 0;
+    if (row_kind(a, r, &n0) != 0) return;
+    // the row's AND / OR / NaN from the per-chunk triples
+    __shared__ uint32_t sh_and[kBigThreads / kWave], sh_or[kBigThreads / kWave];
+    __shared__ uint32_t sh_nan[kBigThreads / kWave];
+    uint32_t av = ~0u, ov = 0u, nv = 0u;
+    for (int i = threadIdx.x; i < chunks; i += kBigThreads) {
+      const u32x4 v = w.ao[(size_t)r * chunks + i];
+      av &= v[0];
+      ov |= v[1];
+      nv |= v[2];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      av &= (uint32_t)__shfl_xor((int)av, m);
+      ov |= (uint32_t)__shfl_xor((int)ov, m);
+      nv |= (uint32_t)__shfl_xor((int)nv, m);
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      sh_and[threadIdx.x >> 6] = av; sh_or[threadIdx.x >> 6] = ov; sh_nan[threadIdx.x >> 6] = nv;
+    }
+    __syncthreads();
+    for (int i = 0; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; nv |= sh_nan[i]; }
+    s = BigState{av, ov, nv, 1u, 0ull, 0, 0, 0, 0, 0, 0};
     const uint32_t diff = s.and_v ^ s.or_v;
     s.shift = diff ? 32 - __builtin_clz(diff) : 0;
     s.P = digit_prefix(s.and_v, s.shift);
@@ -719,11 +754,11 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chun
     s.resolved = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0 && s.nan) raise_fault(a.fault, kFaultNan);
   } else {
-    s = slots[pass];
+    s = slots[pass - 1];
     if (!s.active) return;
     s = pick_digit(s, hrow + (size_t)(pass - 1) * kHistBins, sh_scan, sh_sel);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) slots[pass + 1] = s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) slots[pass] = s;
   if (!refining(s)) return;
   const int n = a.s.q_pos[r] + 1;
   const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
@@ -753,11 +788,11 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chu
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
   BigState* slots = w.st + (size_t)r * kBigSlots;
-  BigState s = slots[kBigPasses];
+  BigState s = slots[kBigPasses - 1];
   if (!s.active) return;
   s = pick_digit(s, w.hist + ((size_t)r * kBigPasses + kBigPasses - 1) * kHistBins, sh_scan,
                  sh_sel);
-  if (blockIdx.x == 0 && threadIdx.x == 0) slots[kBigPasses + 1] = s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) slots[kBigPasses] = s;
   const int shift = s.shift;
   const uint64_t P = s.P;
   const int n = a.s.q_pos[r] + 1;
@@ -793,7 +828,7 @@ __global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chu
   __shared__ int sh_scan[kBigThreads / kWave];
   const int r = blockIdx.y;
   BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[(size_t)r * kBigSlots + kBigPasses + 1];
+  const BigState s = w.st[(size_t)r * kBigSlots + kBigPasses];
   if (!s.active) return;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.len[r] = a.top_k;
   const int shift = s.shift;
@@ -861,7 +896,8 @@ size_t topk_ws_bytes(const SeqView& s, int top_k) {
   const size_t rows = (size_t)s.total_q;
   return round256(rows * kBigSlots * sizeof(BigState)) +
          round256(rows * kBigPasses * kHistBins * 4) +
-         round256(rows * (size_t)big_chunks(s) * 2 * sizeof(int));
+         round256(rows * (size_t)big_chunks(s) * 2 * sizeof(int)) +
+         round256(rows * (size_t)big_chunks(s) * sizeof(u32x4));
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
@@ -872,7 +908,6 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   }
   const int chunks = big_chunks(s);
   const dim3 grid(chunks, s.total_q);
-  k_tkb_init<<<s.total_q, kBigThreads, 0, st>>>(a, chunks);
   k_tkb_andor<<<grid, kBigThreads, 0, st>>>(a, chunks);
   for (int pass = 0; pass < kBigPasses; ++pass)
     k_tkb_hist<<<grid, kBigThreads, 0, st>>>(a, chunks, pass);
