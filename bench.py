@@ -385,8 +385,12 @@ def main():
                     "frac": ach / PEAK_HBM_GBS}
         roof["algorithmic_bytes"] = nbytes
         roof["algorithmic_flops"] = flops
-        roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8<%d, 0>" % rope0,
-                          "topk": "k_topk_cand"}[dom]
+        if case.fmt == "f32":
+            roof["kernel"] = {"indexer": "k_indexer_f32", "mla": "k_mla_f32",
+                              "topk": "k_topk_cand"}[dom]
+        else:
+            roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8<%d, 0>" % rope0,
+                              "topk": "k_topk_cand"}[dom]
         roof["layer"] = l0
         roof["avg_launch_us"] = us
         roof["traffic"] = load_traffic(dom)
