@@ -631,7 +631,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         }
     }
 
-    // ---- online softmax (base 2) per head (lane column), identical in both partner waves
+    // ---- online softmax (base 2) per head (lane column), identical in both partner waves.
+    //      The vector-only phase runs at wave priority 1 (measured 1.5 % faster per tile than
+    //      leaving both waves of a SIMD at one priority; raising the matrix phases instead
+    //      gained nothing).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       // The weights are taken against the running maximum before the tile's own maximum is
@@ -672,6 +676,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
           l_part[ht] += ev[kt][j];
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T over this wave's dim half
