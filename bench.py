@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the side measurements of the bf16-row layout and of "
                          "sliding-window attention")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the side measurement of the step captured into a HIP graph")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused entry instead (no per-kernel events)")
     return ap.parse_args()
@@ -268,6 +270,50 @@ def time_cache_writes(n: int, dev: str, reps: int = 10):
     return out
 
 
+def time_graph_step(run, K: int):
+    """The whole step through the fused entry, eager and captured into one HIP graph, K steps
+    each; the replayed outputs must equal the eager ones bit for bit."""
+    import torch
+
+    def outputs():
+        return [t.clone() for l in sorted(run.out) for t in (run.out[l], run.lse[l])] + \
+               [t.clone() for l in sorted(run.topk_idx) for t in (run.topk_idx[l], run.topk_len[l])]
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    run.run_step(fused=True)
+    torch.cuda.synchronize()
+    ref = outputs()
+    eager_ms = timed(lambda: run.run_step(fused=True))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.run_step(fused=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run_step(fused=True)
+    torch.cuda.synchronize()
+    for l in run.out:
+        run.out[l].fill_(float("nan"))
+    graph_ms = timed(g.replay)
+    got = outputs()
+    same = all(torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+               for a, b in zip(got, ref))
+    del g
+    return {"ms_per_step": graph_ms, "eager_fused_ms_per_step": eager_ms,
+            "bit_identical_to_eager": bool(same), "steps": K}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -395,6 +441,9 @@ def main():
         roof["avg_launch_us"] = us
         roof["traffic"] = load_traffic(dom)
         result["roofline"] = roof
+    if not args.no_graph:
+        result["graph_step"] = time_graph_step(run, K)
+        assert run.fault_bits() == 0, "fault word set during the graph measurement"
     if not args.no_layouts and case.fmt == "fp8":
         result["layouts"] = time_layouts(case, run, dev)
     if args.cache_write_tokens > 0:
