@@ -87,3 +87,63 @@ def test_full_size_workload_sampled_rows(config):
         eo = check_close(go, o, f"{case.name} L{l} out")
         el = check_close(t_np(run.lse[l][rows]), lse, f"{case.name} L{l} lse")
         _say(f"  layer {l}: attention max|d| out {eo:.3e} lse {el:.3e}")
+
+
+def test_full_size_second_layouts_sampled_rows():
+    """The bench's side measurements at the verify workload's full size (its first layer's
+    selections): sparse MLA over a bf16 1,152-B-row cache and over a plain-E4M3 576-B-row
+    cache with FP8 queries, and sliding-window MLA over the last 2,048 positions of the
+    fp8_ds_mla cache -- the same generators and seeds as the bench -- checked on sampled
+    rows against the oracle."""
+    case = synth.config(3, device=DEV)
+    torch.cuda.synchronize()
+    run = CaseRunner(case)
+    d = case.layers[0]
+    l = d["layer"]
+    run.run_layer_split(l)
+    torch.cuda.synchronize()
+    assert run.fault_bits() == 0
+    b = case.batch
+    s = batch_np(b)
+    rows = _sample_rows(s.total_q)
+    H, rope, K = case.mla_heads, d["rope_dim"], d["top_k"]
+    li = case.inputs[l]
+    nb, bs = li.lat_pool.shape[0], li.lat_pool.shape[1]
+    pool16 = synth.make_latent_pool(77, nb, bs, "bf16", device=DEV)
+    pool8, kv_scale = synth.make_plain_e4m3_pool(78, nb, bs, device=DEV)
+    q8, q8s = synth.make_mla_query_fp8(79, b.total_q, H, rope, device=DEV)
+    idx, ln = run.topk_of(l)
+    gi, gl = t_np(idx), t_np(ln)
+    out = torch.empty((b.total_q, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b.total_q, H), dtype=torch.float32, device=DEV)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_MLA, run.seqs, H, K)
+    ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=DEV)
+    fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q_bits = t_np(li.q_mla)
+    win_idx, win_len = O.window_positions(s.q_pos, K)
+    checks = (
+        ("bf16_rows", lambda: M.ml4_sparse_mla_decode(
+            run.seqs, M.make_cache(pool16, M.ML4_LAT_BF16_1152), li.q_mla, M.ML4_BF16, H, rope,
+            idx, ln, K, d["softmax_scale"], d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault),
+         lambda: O.sparse_mla(s, t_np(pool16), "bf16", q_bits, rope, gi, gl,
+                              d["softmax_scale"], d["ssmax_s"], rows=rows)),
+        ("e4m3_rows", lambda: M.ml4_sparse_mla_decode_e4m3(
+            run.seqs, M.make_cache(pool8, M.ML4_LAT_E4M3_576), kv_scale, q8, q8s, H, rope, idx,
+            ln, K, d["softmax_scale"], d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault),
+         lambda: O.sparse_mla(s, t_np(pool8), "e4m3", t_np(q8), rope, gi, gl,
+                              d["softmax_scale"], d["ssmax_s"], rows=rows, q_scale=t_np(q8s),
+                              kv_scale=kv_scale)),
+        ("window2048_fp8", lambda: M.ml4_window_mla_decode(
+            run.seqs, run.lat_caches[l], li.q_mla, M.ML4_BF16, H, rope, K, d["softmax_scale"],
+            d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault),
+         lambda: O.sparse_mla(s, t_np(li.lat_pool), "fp8", q_bits, rope, win_idx, win_len,
+                              d["softmax_scale"], d["ssmax_s"], rows=rows)),
+    )
+    for name, gpu, oracle in checks:
+        gpu()
+        torch.cuda.synchronize()
+        assert M.ml4_fault_query(fault) == 0, name
+        o, ls = oracle()
+        eo = check_close(O.decode_bf16(t_np(out[rows])), o, f"{name} out")
+        el = check_close(t_np(lse[rows]), ls, f"{name} lse")
+        _say(f"  {name}: max|d| out {eo:.3e} lse {el:.3e}")
