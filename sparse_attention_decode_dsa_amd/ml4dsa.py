@@ -65,7 +65,7 @@ def _load() -> C.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
-                          "(python -c 'import __graft_entry__ as g; g.build()')")
+                          "(python -m sparse_attention_decode_dsa_amd.build)")
     lib = C.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
     P = C.POINTER
