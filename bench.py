@@ -158,8 +158,17 @@ def cpu_baseline(case, budget_s: float):
         cores = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:
         cores = os.cpu_count()
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": rows_done / elapsed, "unit": "query-tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{rows_done} query rows ({len(sample)} whole requests), every layer of "
                       f"the step, fp64 numpy oracle; {elapsed:.1f} s of compute"}
 
