@@ -610,3 +610,47 @@ def test_second_layout_writers_round_trip_through_their_readers():
     assert np.all(np.abs(cc8[~inside]) == 448 * kv_scale)
     assert np.all(np.abs(kr8 - O.decode_bf16(rope_bits)) <= np.maximum(
         np.abs(O.decode_bf16(rope_bits)) * 2.0 ** -4, 2.0 ** -10 * kv_scale) * (1 + 1e-6))
+
+
+def test_fp32_format_readers_agree_with_fp8_formats_on_exact_values():
+    """The fp32 cache format (the tiny fp32 decode workload) has its own row readers; holding
+    the exact values of fp8 rows (power-of-two scales, so code x scale is exact in binary32)
+    it must give the fp8 formats' indexer scores and attention.  Pins the fp32 readers and
+    the fp32 query path to the separately pinned fp8 ones."""
+    rng = np.random.default_rng(31)
+    H, n, bs = 5, 37, 8
+    s, nb = _one_request(n, bs=bs)
+    # indexer: e4m3 keys with a power-of-two scale per key, e4m3 queries with power-of-two
+    # per-head scales
+    ipool = P.index_pool(nb, bs)
+    flat = ipool.reshape(-1, 132)
+    codes = rng.integers(0, 256, size=(nb * bs, 128), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x22
+    flat[:, :128] = codes
+    ks = np.exp2(rng.integers(-6, 3, size=nb * bs)).astype(np.float32)
+    flat[:, 128:] = np.frombuffer(ks.astype("<f4").tobytes(), np.uint8).reshape(-1, 4)
+    qc = rng.integers(0, 256, size=(1, H, 128), dtype=np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x41
+    qs = np.exp2(rng.integers(-4, 4, size=(1, H))).astype(np.float32)
+    w = rng.uniform(-1, 1, size=(1, H)).astype(np.float32)
+    ref = O.indexer_scores(s, ipool, "fp8", qc, qs, w, 0.25, n)
+    kf = (O.decode_e4m3(codes) * ks[:, None]).astype(np.float32)            # exact
+    ipool32 = kf.reshape(nb, bs, 128)
+    q32 = (O.decode_e4m3(qc) * qs[..., None]).astype(np.float32)            # exact
+    got = O.indexer_scores(s, ipool32, "f32", q32, None, w, 0.25, n)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0)
+    # attention: fp8_ds_mla rows with power-of-two group scales, bf16 RoPE, bf16 queries
+    s2, pool, q = _random_latent_case(n, H, 64, 32)
+    lat = pool.reshape(-1, 656)
+    sc = np.exp2(rng.integers(-9, -4, size=(lat.shape[0], 4))).astype("<f4")
+    lat[:, 512:528] = np.frombuffer(sc.tobytes(), np.uint8).reshape(-1, 16)
+    sel = np.array([[0, 3, 8, 9, 20, 36, -1, -1]])
+    ln = np.array([6])
+    o8, l8 = O.sparse_mla(s2, pool, "fp8", q, 64, sel, ln, 0.05, 0.3)
+    c, kr = O.latent_rows_fp8(pool, np.arange(lat.shape[0]), 64)
+    pool32 = np.concatenate([c, kr], axis=1).astype(np.float32).reshape(pool.shape[0], pool.shape[1], 576)
+    assert np.array_equal(pool32.reshape(-1, 576).astype(np.float64), np.concatenate([c, kr], 1))
+    q32m = O.decode_bf16(q).astype(np.float32)
+    o32, l32 = O.sparse_mla(s2, pool32, "f32", q32m, 64, sel, ln, 0.05, 0.3)
+    assert np.allclose(o32, o8, rtol=1e-12, atol=1e-15)
+    assert np.allclose(l32, l8, rtol=1e-12, atol=0)
