@@ -267,6 +267,147 @@ void k_indexer_fp8(IndexerLaunch a, int groups_per_seq, int keys_per_wg) {
   }
 }
 
+// One query row per work-group (decode): with a single row there is nothing to share, so
+// each key is decoded once in any case and the LDS staging, with its barrier per step, is
+// pure latency.  Here every wave scores its own 64-key blocks (w, w + 4, ... of the chunk)
+// straight from HBM: lane (g, c) loads the 32 bytes of key c that hold dims 32 g .. 32 g + 31
+// -- exactly its B-operand fragment -- decodes them in registers and multiplies; the next
+// block's loads are in flight meanwhile.  No barrier after the block table.  The arithmetic
+// (fragment dims, MFMA order, head reduction, transpose-sum) is that of k_indexer_fp8, so
+// the scores are bit-identical.
+template <int HT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_indexer_row(IndexerLaunch a, int keys_per_wg) {
+  __shared__ int blk_sh[kMaxKeysPerWg / 16];   // block of each 16-key group of the chunk
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int g16 = lane >> 4;
+  const int c16 = lane & 15;
+  const SeqView& s = a.s;
+  const int b = blockIdx.y;
+  const int row = s.q_start[b];
+  if (s.q_start[b + 1] - row <= 0) return;
+  const int seq_len = s.seq_lens[b];
+  const int k_lo = blockIdx.x * keys_per_wg;
+  const int k_hi = min(k_lo + keys_per_wg, s.max_seq_len);
+  if (k_lo >= k_hi) return;
+  int pos = s.q_pos[row];
+  if (pos < 0 || pos >= seq_len || pos >= s.max_seq_len) {
+    if (blockIdx.x == 0 && tid == 0) raise_fault(a.fault, 1u << 3);
+    pos = -1;
+  }
+  const int32_t* bt = s.block_table + (size_t)b * s.mbps;
+  const int k_end = min(k_hi, pos + 1);          // keys scored: k_lo .. k_end - 1
+  for (int gi = tid; gi * 16 < k_end - k_lo; gi += kThreads) {
+    const int blk = bt[(k_lo + 16 * gi) >> s.lbs];
+    if ((unsigned)blk >= (unsigned long long)a.num_blocks) {
+      raise_fault(a.fault, 1u << 0);
+      blk_sh[gi] = -1;
+    } else {
+      blk_sh[gi] = blk;
+    }
+  }
+
+  f16x8 qa[HT][4];
+  float wq[HT][4];
+  const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint8_t* qp = qbase + ((size_t)row * a.n_heads + ht * 16 + c16) * 128 + 32 * g16;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(qp);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(qp + 16);
+    const uint32_t w8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x4 lo = e4m3x4_to_f16(w8[2 * c]);
+      const f16x4 hi = e4m3x4_to_f16(w8[2 * c + 1]);
+      qa[ht][c] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = (size_t)row * a.n_heads + ht * 16 + 4 * g16 + i;
+      wq[ht][i] = a.w[o] * (a.q_scale ? a.q_scale[o] : 1.0f);
+    }
+  }
+  const float mrow = ssmax_mult(a.ssmax_s, max(pos, 0));
+  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
+  const int bs_mask = (1 << s.lbs) - 1;
+  const float ninf = -__builtin_inff();
+  float* srow = a.scores + (size_t)row * a.ld;
+
+  for (int t = max(k_lo, k_end) + tid; t < k_hi; t += kThreads) srow[t] = ninf;
+  const int nblk = (k_end - k_lo + 63) / 64;     // 64-key blocks holding scored keys
+  __syncthreads();   // blk_sh
+  if (wave >= nblk) return;
+
+  // Sub-tile j of block m: keys k_lo + 64 (wave + 4 m) + 16 j + c; lane (g, c) holds key c.
+  struct Frag {
+    u32x4 lo, hi;
+    float scale;
+    int ok;
+  };
+  auto load = [&](Frag& F, int m, int j) {
+    F.lo = u32x4{0, 0, 0, 0};
+    F.hi = u32x4{0, 0, 0, 0};
+    F.scale = 0.f;
+    F.ok = 0;
+    const int t = k_lo + 64 * (wave + 4 * m) + 16 * j + c16;
+    if (wave + 4 * m >= nblk || t >= k_end) return;
+    const int blk = blk_sh[(t - k_lo) >> 4];
+    if (blk < 0) return;
+    const uint8_t* rp = pool + (((int64_t)blk << s.lbs) + (t & bs_mask)) * kIdxRow;
+    const u32x4a4 v0 = *reinterpret_cast<const u32x4a4*>(rp + 32 * g16);
+    const u32x4a4 v1 = *reinterpret_cast<const u32x4a4*>(rp + 32 * g16 + 16);
+    F.lo = u32x4{v0[0], v0[1], v0[2], v0[3]};
+    F.hi = u32x4{v1[0], v1[1], v1[2], v1[3]};
+    F.scale = *reinterpret_cast<const float*>(rp + 128);
+    F.ok = 1;
+  };
+  Frag f0, f1, f2, f3;
+  load(f0, 0, 0);
+  load(f1, 0, 1);
+  load(f2, 0, 2);
+  load(f3, 0, 3);
+  for (int m = 0; wave + 4 * m < nblk; ++m) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float keep_scale = 0.f;    // of sub-tile g16's key c16 (this lane's column after the sum)
+    int keep_ok = 0;
+    auto sub = [&](Frag& F, int j) {
+      const uint32_t w8[8] = {F.lo[0], F.lo[1], F.lo[2], F.lo[3],
+                              F.hi[0], F.hi[1], F.hi[2], F.hi[3]};
+      if (g16 == j) {
+        keep_scale = F.scale;
+        keep_ok = F.ok;
+      }
+      f16x8 kb[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f16x4 lo = e4m3x4_to_f16(w8[2 * c]);
+        const f16x4 hi = e4m3x4_to_f16(w8[2 * c + 1]);
+        kb[c] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      load(F, m + 1, j);       // the next block's sub-tile j, in flight while this block runs
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4 d{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) d = mfma_f16(qa[ht][c], kb[c], d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[j] = fmaf(wq[ht][i], relu_bits(d[i]), part[j]);
+      }
+    };
+    sub(f0, 0);
+    sub(f1, 1);
+    sub(f2, 2);
+    sub(f3, 3);
+    const float tot = sum_over_lane_groups(part);
+    const int t = k_lo + 64 * (wave + 4 * m) + 16 * g16 + c16;
+    if (t < k_hi) srow[t] = (t < k_end && keep_ok) ? tot * keep_scale * mrow : ninf;
+  }
+}
+
 // fp32 format: 128 x fp32 per key, no key scale, fp32 queries.  One thread per key, the
 // row's queries in LDS.
 __global__ __launch_bounds__(256) void k_indexer_f32(IndexerLaunch a) {
@@ -319,6 +460,16 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerLaunch a) {
 
 template <int R>
 hipError_t dispatch_heads(const IndexerLaunch& a, dim3 grid, int gps, int kpw, hipStream_t st) {
+  if constexpr (R == 1) {
+    switch (a.n_heads / 16) {
+      case 1: k_indexer_row<1><<<grid, kThreads, 0, st>>>(a, kpw); break;
+      case 2: k_indexer_row<2><<<grid, kThreads, 0, st>>>(a, kpw); break;
+      case 3: k_indexer_row<3><<<grid, kThreads, 0, st>>>(a, kpw); break;
+      case 4: k_indexer_row<4><<<grid, kThreads, 0, st>>>(a, kpw); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.n_heads / 16) {
     case 1: k_indexer_fp8<R, 1><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
     case 2: k_indexer_fp8<R, 2><<<grid, kThreads, 0, st>>>(a, gps, kpw); break;
