@@ -8,7 +8,7 @@ data drawn on the GPU and resident in HBM before timing starts.
 
 One step = for each layer: indexer scores -> exact top-k -> sparse MLA (the three entry
 points the fused entry chains), timed with HIP events on the launch stream.
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: the benchmark runs on one GPU.
 """
 
 from __future__ import annotations

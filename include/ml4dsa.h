@@ -41,7 +41,7 @@ typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 enum ml4_status {
   ML4_OK = 0,
   ML4_E_INVALID = -1,       /* an argument is out of its documented range       */
-  ML4_E_UNSUPPORTED = -2,   /* a valid combination this build does not provide   */
+  ML4_E_UNSUPPORTED = -2,   /* a valid combination the library does not provide  */
   ML4_E_WORKSPACE = -3,     /* ws_bytes below ml4_workspace_bytes()              */
   ML4_E_LAUNCH = -4,        /* the HIP runtime refused a launch                  */
   ML4_E_DEVICE_FAULT = -5   /* ml4_fault_query found fault bits set              */
