@@ -58,6 +58,9 @@ def small_cases():
         "r2_verify_ragged": synth.make_case(
             "r2v", 71, seq_lens=[9001, 17000, 3], q_per_seq=[2, 2, 1], block_size=64,
             fmt="fp8", idx_heads=64, mla_heads=128, layers=[L(0, ssmax_s=0.3)]),
+        "h48_decode_rows": synth.make_case(
+            "h48", 81, seq_lens=[3001, 700, 4500], q_per_seq=[1, 1, 1], block_size=32,
+            fmt="fp8", idx_heads=48, mla_heads=32, layers=[L(0, top_k=1024, idx_ssmax_s=0.2)]),
         "h16_h64_blocks16": synth.make_case(
             "hx", 61, seq_lens=[900, 1500], q_per_seq=[2, 1], block_size=16, fmt="fp8",
             idx_heads=32, mla_heads=16, layers=[L(0, top_k=512, idx_ssmax_s=0.25)]),
@@ -108,7 +111,8 @@ def test_layer_step_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["c1_fp32_4096", "c2_decode_ragged", "c3_verify_rope_nope",
-                                  "c5_prefill_causal", "r2_verify_ragged", "h16_h64_blocks16"])
+                                  "c5_prefill_causal", "r2_verify_ragged", "h48_decode_rows",
+                                  "h16_h64_blocks16"])
 def test_indexer_scores_match_oracle(name):
     case = CASES[name]
     _say(f"[gpu] indexer {name}")
