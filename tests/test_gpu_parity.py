@@ -61,6 +61,12 @@ def small_cases():
         "h48_decode_rows": synth.make_case(
             "h48", 81, seq_lens=[3001, 700, 4500], q_per_seq=[1, 1, 1], block_size=32,
             fmt="fp8", idx_heads=48, mla_heads=32, layers=[L(0, top_k=1024, idx_ssmax_s=0.2)]),
+        "h16_decode_rows": synth.make_case(
+            "h16d", 83, seq_lens=[2500, 130], q_per_seq=[1, 1], block_size=64,
+            fmt="fp8", idx_heads=16, mla_heads=16, layers=[L(0, top_k=512)]),
+        "h32_decode_rows": synth.make_case(
+            "h32d", 85, seq_lens=[5100], q_per_seq=[1], block_size=16,
+            fmt="fp8", idx_heads=32, mla_heads=48, layers=[L(0, top_k=2048)]),
         "h16_h64_blocks16": synth.make_case(
             "hx", 61, seq_lens=[900, 1500], q_per_seq=[2, 1], block_size=16, fmt="fp8",
             idx_heads=32, mla_heads=16, layers=[L(0, top_k=512, idx_ssmax_s=0.25)]),
@@ -112,7 +118,7 @@ def test_layer_step_matches_oracle(name):
 
 @pytest.mark.parametrize("name", ["c1_fp32_4096", "c2_decode_ragged", "c3_verify_rope_nope",
                                   "c5_prefill_causal", "r2_verify_ragged", "h48_decode_rows",
-                                  "h16_h64_blocks16"])
+                                  "h16_decode_rows", "h32_decode_rows", "h16_h64_blocks16"])
 def test_indexer_scores_match_oracle(name):
     case = CASES[name]
     _say(f"[gpu] indexer {name}")
