@@ -253,6 +253,8 @@ def indexer_scores(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray,
     fmt 'f32': q is float32 [total_q, H, 128], pool float32 [nb, bs, 128].
     q_scale [total_q, H] (None = 1), w [total_q, H].
     """
+    if fmt not in ("fp8", "f32"):
+        raise ValueError(f"indexer_scores: unknown index format {fmt!r}")
     rows = range(seqs.total_q) if rows is None else rows
     out = np.full((len(rows), ld), -np.inf)
     for i, r in enumerate(rows):
@@ -315,8 +317,13 @@ def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: 
     fmt 'e4m3': pool uint8 [nb, bs, 576] plain E4M3 rows times kv_scale; q uint8 E4M3 codes
                 [total_q, H, 512 + rope_dim] times q_scale [total_q, H].
     fmt 'f32': pool float32 [nb, bs, 576]; q float32 [total_q, H, 512 + rope_dim].
-    topk_idx holds logical positions; entries past topk_len[r] are ignored.
+    topk_idx holds logical positions; entries past topk_len[r] are ignored.  Any other
+    format is refused.
     """
+    if fmt not in ("fp8", "bf16", "e4m3", "f32"):
+        raise ValueError(f"sparse_mla: unknown latent format {fmt!r}")
+    if fmt == "e4m3" and q_scale is None:
+        raise ValueError("sparse_mla: the 'e4m3' format needs q_scale")
     rows = range(seqs.total_q) if rows is None else rows
     H = q.shape[1]
     o = np.zeros((len(rows), H, KV_LORA))
@@ -353,21 +360,40 @@ def sparse_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: 
 
 def dense_mla(seqs: Seqs, pool: np.ndarray, fmt: str, q: np.ndarray, rope_dim: int,
               softmax_scale: float, ssmax_s: float,
-              rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+              rows: Optional[Sequence[int]] = None, q_scale: Optional[np.ndarray] = None,
+              kv_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """Dense MLA over every visible key t in [0, q_pos[r]]: softmax(sigma Q K^T) V with
     K = [c | kr] and V = c, written as whole-matrix products.  Equals sparse_mla whenever
-    the selection holds every visible key (top_k >= context)."""
+    the selection holds every visible key (top_k >= context).
+
+    Formats and query types as sparse_mla: 'fp8' (656-B rows, bf16 q), 'bf16' (1,152-B
+    rows, bf16 q), 'e4m3' (576-B plain E4M3 rows times kv_scale, E4M3 q times q_scale
+    [total_q, H]), 'f32' (fp32 rows and q).  Any other format is refused."""
+    if fmt not in ("fp8", "bf16", "e4m3", "f32"):
+        raise ValueError(f"dense_mla: unknown latent format {fmt!r}")
+    if fmt == "e4m3" and q_scale is None:
+        raise ValueError("dense_mla: the 'e4m3' format needs q_scale")
     rows = range(seqs.total_q) if rows is None else rows
     H = q.shape[1]
     o = np.zeros((len(rows), H, KV_LORA))
     lse = np.zeros((len(rows), H))
-    dec = {"fp8": latent_rows_fp8, "bf16": latent_rows_bf16}.get(fmt, latent_rows_f32)
     for i, r in enumerate(rows):
         b = seqs.request_of(r)
         p = int(seqs.q_pos[r])
-        c, kr = dec(pool, slots(seqs, b, np.arange(p + 1)), rope_dim)
+        sl = slots(seqs, b, np.arange(p + 1))
+        if fmt == "fp8":
+            c, kr = latent_rows_fp8(pool, sl, rope_dim)
+            qv = decode_bf16(q[r])
+        elif fmt == "bf16":
+            c, kr = latent_rows_bf16(pool, sl, rope_dim)
+            qv = decode_bf16(q[r])
+        elif fmt == "e4m3":
+            c, kr = latent_rows_e4m3(pool, sl, rope_dim, kv_scale)
+            qv = decode_e4m3(q[r]) * np.asarray(q_scale[r], dtype=np.float64)[:, None]
+        else:
+            c, kr = latent_rows_f32(pool, sl, rope_dim)
+            qv = np.asarray(q[r], np.float64)
         K = np.concatenate([c, kr], axis=1)               # [n, 512 + rope]
-        qv = decode_bf16(q[r]) if fmt in ("fp8", "bf16") else np.asarray(q[r], np.float64)
         Q = qv[:, :KV_LORA + rope_dim]
         S = softmax_scale * ssmax_multiplier(ssmax_s, p) * (Q @ K.T)
         mx = S.max(axis=1)

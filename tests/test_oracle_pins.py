@@ -319,6 +319,52 @@ def test_mla_full_selection_equals_library_attention(rope_dim):
     assert np.allclose(lsed[0], lse[0], rtol=1e-13)
 
 
+@pytest.mark.parametrize("rope_dim", [64, 0])
+def test_dense_mla_f32_and_plain_e4m3_formats_equal_library_attention(rope_dim):
+    """dense_mla's fp32 and plain-E4M3 branches (queries times per-head scales, rows times
+    the per-tensor scale) against torch's float64 scaled-dot-product attention on the
+    decoded values, and against sparse_mla with every visible key selected."""
+    g = np.random.default_rng(51)
+    n, H = 45, 6
+    seqs = O.Seqs(np.array([n]), np.array([0, 2]), np.array([30, n - 1]),
+                  np.arange(1)[None, :], n)
+    scale = 1.0 / math.sqrt(512 + rope_dim)
+    rows32 = g.normal(size=(1, n, 576)).astype(np.float32)
+    q32 = g.normal(size=(2, H, 512 + rope_dim)).astype(np.float32)
+    codes = g.integers(0, 256, (1, n, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x05
+    qc = g.integers(0, 256, (2, H, 512 + rope_dim)).astype(np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x3A
+    qs = g.uniform(0.01, 0.02, size=(2, H))
+    kv_scale = 0.0123
+    cases = [("f32", rows32, q32, {},
+              rows32[0].astype(np.float64), q32.astype(np.float64)),
+             ("e4m3", codes, qc, {"q_scale": qs, "kv_scale": kv_scale},
+              O.E4M3_TABLE[codes[0]] * kv_scale, O.E4M3_TABLE[qc] * qs[..., None])]
+    for fmt, pool, q, kw, rows_v, q_v in cases:
+        od, ld_ = O.dense_mla(seqs, pool, fmt, q, rope_dim, scale, 0.0, **kw)
+        idx, ln = O.window_positions(seqs.q_pos, 64)
+        os_, ls_ = O.sparse_mla(seqs, pool, fmt, q, rope_dim, idx, ln, scale, 0.0, **kw)
+        assert np.allclose(od, os_, rtol=1e-12, atol=1e-14) and np.allclose(ld_, ls_, rtol=1e-13)
+        for r in range(2):
+            m = int(seqs.q_pos[r]) + 1
+            K = torch.from_numpy(np.concatenate([rows_v[:m, :512], rows_v[:m, 512:512 + rope_dim]],
+                                                axis=1))[None, None].expand(1, H, m, -1)
+            V = torch.from_numpy(np.ascontiguousarray(rows_v[:m, :512]))[None, None].expand(1, H, m, -1)
+            Q = torch.from_numpy(np.ascontiguousarray(q_v[r]))[None, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[0, :, 0]
+            assert np.allclose(od[r], ref.numpy(), rtol=1e-10, atol=1e-12), fmt
+            lref = torch.logsumexp(scale * (Q[0, :, 0] @ K[0, 0].T), dim=1).numpy()
+            assert np.allclose(ld_[r], lref, rtol=1e-12), fmt
+    with pytest.raises(ValueError):
+        O.dense_mla(seqs, codes, "e4m3", qc, rope_dim, scale, 0.0)          # no q_scale
+    with pytest.raises(ValueError):
+        O.dense_mla(seqs, rows32, "fp16", q32, rope_dim, scale, 0.0)        # unknown format
+    with pytest.raises(ValueError):
+        O.sparse_mla(seqs, rows32, "fp16", q32, rope_dim, np.zeros((2, 1), np.int64),
+                     np.ones(2, np.int64), scale, 0.0)
+
+
 def test_mla_ssmax_and_order_invariance_and_nope_rope_bytes():
     n, H = 50, 4
     s, pool, q = _random_latent_case(n, H, 64, 9)
@@ -382,6 +428,52 @@ def test_layer_modes_consumer_and_shared_indexer():
     o2, l2, i2, _ = O.layer_step(L2, s, "fp8", {0: pool0, 1: pool1}, {2: ipool}, qi, None, w,
                                  q, store, ld=64)
     assert np.array_equal(o2, o0) and np.array_equal(i2, i0)   # same indexer inputs here
+
+
+def test_consumer_layer_runs_its_own_indexer_on_the_owner_cache():
+    """A KV-sharing consumer keeps its own indexer [blog, 跨层 KV 共享: only the latent cache
+    is shared]: with indexer inputs unlike the owner's, its top-k is the top-k of its own
+    scores (recomputed here from the definition, not taken from the owner), its attention
+    reads the owner's latent rows, and a NaN-filled latent pool under its own layer number
+    is never read."""
+    n, H, Hi, bs, k = 96, 4, 2, 8, 12
+    s, pool0, q = _random_latent_case(n, H, 64, 41, bs=bs)
+    nb = pool0.shape[0]
+    g = np.random.default_rng(42)
+
+    def ipool_of(seed):
+        r = np.random.default_rng(seed)
+        ip = r.integers(0, 256, size=(nb, bs, 132), dtype=np.uint8)
+        ip[:, :, :128][(ip[:, :, :128] & 0x7F) == 0x7F] = 0
+        ip.reshape(-1, 132)[:, 128:] = np.frombuffer(
+            r.uniform(0.5, 2.0, nb * bs).astype("<f4").tobytes(), np.uint8).reshape(-1, 4)
+        return ip
+
+    ip0, ip2 = ipool_of(43), ipool_of(44)
+    qi0 = g.integers(0, 0x70, size=(1, Hi, 128), dtype=np.uint8)
+    qi2 = g.integers(0, 0x70, size=(1, Hi, 128), dtype=np.uint8)
+    w0, w2 = g.uniform(size=(1, Hi)), g.uniform(size=(1, Hi))
+    nan_pool = np.full_like(pool0, 0x7F)                       # every code NaN
+    lat = {0: pool0, 2: nan_pool}
+    store = {}
+    o0, l0, i0, n0 = O.layer_step(O.Layer(0, top_k=k), s, "fp8", lat, {0: ip0}, qi0, None, w0,
+                                  q, store, ld=n)
+    L2 = O.Layer(2, kv_sharing_target_layer=0, top_k=k)
+    o2, l2, i2, n2 = O.layer_step(L2, s, "fp8", lat, {2: ip2}, qi2, None, w2, q, store, ld=n)
+    # the consumer's own selection, from its own scores by brute-force sorting
+    p = int(s.q_pos[0])
+    sc = np.zeros(p + 1)
+    for t in range(p + 1):
+        kv, ks = O.index_rows_fp8(ip2, O.slots(s, 0, np.array([t])))
+        dots = O.decode_e4m3(qi2[0]) @ kv[0]
+        sc[t] = ks[0] * float(np.sum(w2[0] * np.maximum(dots, 0.0)))
+    want = sorted(sorted(range(p + 1), key=lambda t: (-sc[t], t))[:k])
+    assert list(i2[0][:k]) == want and n2[0] == k
+    assert not np.array_equal(i2, i0), "inputs chosen so that the two selections differ"
+    assert 2 in store and np.array_equal(store[2][0], i2)
+    ref = O.sparse_mla(s, pool0, "fp8", q, 64, i2, n2, L2.softmax_scale, 0.0)
+    assert np.array_equal(o2, ref[0]) and np.array_equal(l2, ref[1])
+    assert np.all(np.isfinite(o2)) and not np.allclose(o2, o0)
 
 
 # ---------------------------------------------------------------- KV-cache writes (quantiser)
