@@ -36,7 +36,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 
-#define ML4_ABI_VERSION 4
+#define ML4_ABI_VERSION 5
 
 enum ml4_status {
   ML4_OK = 0,
@@ -248,20 +248,27 @@ typedef struct {
  * synchronisation.  [blog, ROCm implementation details › 专用解码 (the whole indexer, exact
  * top-2048 and sparse MLA inside one launch per layer, with NoPE, KV-sharing and
  * index-sharing layers)]
+ *   layers: [host] array of n_layers descriptors, indexed by layer (layers[i].layer == i
+ *   for this layer and every layer it names); the call runs layer `layer`.
  *   lat_caches, idx_caches: [host] arrays of n_layers caches, indexed by layer.
  *   topk_bufs, topk_lens: [host] arrays of n_layers device pointers, indexed by layer.
  *   An indexer layer (topk_source_layer < 0) scores idx_caches[layer], selects, and writes
- *   topk_bufs[layer] / topk_lens[layer]; a shared-indexer layer reads
+ *   topk_bufs[layer] ([total_q][top_k]) / topk_lens[layer]; a shared-indexer layer reads
  *   topk_bufs[topk_source_layer] and runs no indexer.  The attention reads
  *   lat_caches[kv_sharing_target_layer >= 0 ? kv_sharing_target_layer : layer].
+ *   Layer roles are validated from the descriptors [blog, 跨层 KV 共享; Model architecture]:
+ *   the KV-sharing target must own its cache (its own kv_sharing_target_layer is -1: no
+ *   chains); the top-k source must run its own indexer (its topk_source_layer is -1) and
+ *   have the same top_k (the row stride of the shared buffer).  Both must be earlier layers.
  *   q_idx/q_idx_scale/w_idx as in ml4_indexer_score (ignored for a shared-indexer layer);
  *   q_mla/out/lse as in ml4_sparse_mla_decode.
  *   ws: ml4_workspace_bytes(ML4_ENTRY_LAYER, s, mla_heads, top_k) bytes (holds the scores).
  */
-int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache* lat_caches,
-                          const ml4_cache* idx_caches, int32_t n_layers, const void* q_idx,
-                          int32_t q_idx_dtype, const float* q_idx_scale, const float* w_idx,
-                          const void* q_mla, int32_t q_mla_dtype, int32_t* const* topk_bufs,
+int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                          const ml4_cache* lat_caches, const ml4_cache* idx_caches,
+                          int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
+                          const float* q_idx_scale, const float* w_idx, const void* q_mla,
+                          int32_t q_mla_dtype, int32_t* const* topk_bufs,
                           int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
                           void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream);
 

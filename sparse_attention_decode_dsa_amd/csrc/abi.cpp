@@ -368,27 +368,46 @@ int ml4_window_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   return launch_status(ml4::launch_mla(a, stream), "ml4_window_mla_decode");
 }
 
-int ml4_sparse_attn_layer(const ml4_layer* L, const ml4_seqs* s, const ml4_cache* lat_caches,
-                          const ml4_cache* idx_caches, int32_t n_layers, const void* q_idx,
-                          int32_t q_idx_dtype, const float* q_idx_scale, const float* w_idx,
-                          const void* q_mla, int32_t q_mla_dtype, int32_t* const* topk_bufs,
+int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                          const ml4_cache* lat_caches, const ml4_cache* idx_caches,
+                          int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
+                          const float* q_idx_scale, const float* w_idx, const void* q_mla,
+                          int32_t q_mla_dtype, int32_t* const* topk_bufs,
                           int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
                           void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream) {
   Checks c;
   check_seqs(c, s);
-  c.bad(L == nullptr, "layer descriptor is NULL");
+  c.bad(layers == nullptr, "layers is NULL");
   c.bad(n_layers < 1, "n_layers must be >= 1");
   c.bad(!lat_caches || !topk_bufs || !topk_lens, "lat_caches, topk_bufs, topk_lens must be non-NULL");
-  if (!L || n_layers < 1 || !lat_caches || !topk_bufs || !topk_lens) return c.finish("ml4_sparse_attn_layer");
-  const int l = L->layer;
-  c.bad(l < 0 || l >= n_layers, "layer outside 0 .. n_layers-1");
-  const int tgt = L->kv_sharing_target_layer, src = L->topk_source_layer;
-  c.bad(tgt != -1 && (tgt < 0 || tgt >= l),
-        "kv_sharing_target_layer must be -1 or an earlier layer");
-  c.bad(src != -1 && (src < 0 || src >= l), "topk_source_layer must be -1 or an earlier layer");
-  if (l < 0 || l >= n_layers || (tgt != -1 && (tgt < 0 || tgt >= l)) ||
-      (src != -1 && (src < 0 || src >= l)))
+  c.bad(layer < 0 || layer >= n_layers, "layer outside 0 .. n_layers-1");
+  if (!layers || n_layers < 1 || !lat_caches || !topk_bufs || !topk_lens || layer < 0 ||
+      layer >= n_layers)
     return c.finish("ml4_sparse_attn_layer");
+  const ml4_layer* L = &layers[layer];
+  const int l = layer;
+  c.bad(L->layer != l, "layers[layer].layer differs from layer");
+  const int tgt = L->kv_sharing_target_layer, src = L->topk_source_layer;
+  const bool tgt_ok = tgt == -1 || (tgt >= 0 && tgt < l);
+  const bool src_ok = src == -1 || (src >= 0 && src < l);
+  c.bad(!tgt_ok, "kv_sharing_target_layer must be -1 or an earlier layer");
+  c.bad(!src_ok, "topk_source_layer must be -1 or an earlier layer");
+  if (!tgt_ok || !src_ok) return c.finish("ml4_sparse_attn_layer");
+  // [blog, 跨层 KV 共享]: a consumer reads the cache of a layer that owns one (no chains);
+  // [blog, Model architecture]: a shared-indexer layer reuses the top-k of a layer that runs
+  // its own indexer, with the same top_k (the row stride of that layer's top-k buffer).
+  if (tgt >= 0) {
+    c.bad(layers[tgt].layer != tgt, "layers[kv_sharing_target_layer].layer differs from its index");
+    c.bad(layers[tgt].kv_sharing_target_layer != -1,
+          "kv_sharing_target_layer names a consumer layer: the target must own its cache");
+  }
+  if (src >= 0) {
+    c.bad(layers[src].layer != src, "layers[topk_source_layer].layer differs from its index");
+    c.bad(layers[src].topk_source_layer != -1,
+          "topk_source_layer names a shared-indexer layer: the source must run its own indexer");
+    c.bad(layers[src].top_k != L->top_k,
+          "top_k differs from the topk_source_layer's top_k (the shared top-k rows' stride)");
+  }
   const int lat_layer = tgt >= 0 ? tgt : l;
   const bool own_indexer = src < 0;
   const int topk_layer = own_indexer ? l : src;

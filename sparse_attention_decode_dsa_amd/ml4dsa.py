@@ -12,11 +12,10 @@ import os
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# ML4DSA_LIB selects another build of the same library (A/B timing); default: in-tree build.
-LIB_PATH = os.environ.get("ML4DSA_LIB") or os.path.join(PKG, "libml4dsa.so")
+LIB_PATH = os.path.join(PKG, "libml4dsa.so")
 
 # ---- constants mirrored from include/ml4dsa.h
-ML4_ABI_VERSION = 4
+ML4_ABI_VERSION = 5
 ML4_OK, ML4_E_INVALID, ML4_E_UNSUPPORTED, ML4_E_WORKSPACE, ML4_E_LAUNCH, ML4_E_DEVICE_FAULT = (
     0, -1, -2, -3, -4, -5)
 ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
@@ -90,7 +89,7 @@ def _load() -> C.CDLL:
                                                vp, vp, i32, f32, f32, vp, i32, vp, vp, sz, vp,
                                                vp]
     lib.ml4_sparse_attn_layer.restype = C.c_int
-    lib.ml4_sparse_attn_layer.argtypes = [P(ml4_layer), P(ml4_seqs), P(ml4_cache),
+    lib.ml4_sparse_attn_layer.argtypes = [P(ml4_layer), i32, P(ml4_seqs), P(ml4_cache),
                                           P(ml4_cache), i32, vp, i32, vp, vp, vp, i32,
                                           P(vp), P(vp), vp, i32, vp, vp, sz, vp, vp]
     lib.ml4_index_cache_write.restype = C.c_int
@@ -224,17 +223,18 @@ def ml4_sparse_mla_decode_e4m3(seqs, kv, kv_scale, q, q_scale, n_heads, rope_dim
     return _check(rc) if check else rc
 
 
-def ml4_sparse_attn_layer(layer: ml4_layer, seqs, lat_caches: Sequence[ml4_cache],
-                          idx_caches: Sequence[ml4_cache], q_idx, q_idx_dtype, q_idx_scale,
-                          w_idx, q_mla, q_mla_dtype, topk_bufs, topk_lens, out, out_dtype,
-                          lse=None, ws=None, ws_bytes=0, fault=None, stream=None,
-                          check=True) -> int:
+def ml4_sparse_attn_layer(layers: Sequence[ml4_layer], layer: int, seqs,
+                          lat_caches: Sequence[ml4_cache], idx_caches: Sequence[ml4_cache],
+                          q_idx, q_idx_dtype, q_idx_scale, w_idx, q_mla, q_mla_dtype,
+                          topk_bufs, topk_lens, out, out_dtype, lse=None, ws=None, ws_bytes=0,
+                          fault=None, stream=None, check=True) -> int:
     n = len(lat_caches)
+    descs = (ml4_layer * n)(*layers)
     lat = (ml4_cache * n)(*lat_caches)
     idx = (ml4_cache * n)(*idx_caches)
     bufs = (C.c_void_p * n)(*[ptr(b) for b in topk_bufs])
     lens = (C.c_void_p * n)(*[ptr(b) for b in topk_lens])
-    rc = LIB.ml4_sparse_attn_layer(C.byref(layer), C.byref(seqs), lat, idx, n, ptr(q_idx),
+    rc = LIB.ml4_sparse_attn_layer(descs, layer, C.byref(seqs), lat, idx, n, ptr(q_idx),
                                    q_idx_dtype, ptr(q_idx_scale), ptr(w_idx), ptr(q_mla),
                                    q_mla_dtype, bufs, lens, ptr(out), out_dtype, ptr(lse), ptr(ws),
                                    ws_bytes, ptr(fault), stream_handle(stream))

@@ -71,6 +71,16 @@ class CaseRunner:
             self.lse[l] = torch.empty((T, case.mla_heads), dtype=torch.float32, device=dev)
             ws = max(ws, M.ml4_workspace_bytes(M.ML4_ENTRY_LAYER, self.seqs, case.mla_heads,
                                                d["top_k"]))
+        # descriptors of every layer index, in order (an index the case does not run gets
+        # an owner descriptor that no call names)
+        self.layers: List[M.ml4_layer] = []
+        for i in range(self.n_layers):
+            if i in self.desc:
+                self.layers.append(self.desc[i])
+            else:
+                D = M.ml4_layer()
+                D.layer, D.kv_sharing_target_layer, D.topk_source_layer = i, -1, -1
+                self.layers.append(D)
         self.ld = (b.max_seq_len + 3) // 4 * 4
         self.ws_bytes = max(ws, 256)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
@@ -103,10 +113,10 @@ class CaseRunner:
 
     def run_layer_fused(self, l: int, stream=None):
         li = self.case.inputs[l]
-        L = self.desc[l]
         bufs = [self.topk_idx.get(i) for i in range(self.n_layers)]
         lens = [self.topk_len.get(i) for i in range(self.n_layers)]
-        M.ml4_sparse_attn_layer(L, self.seqs, self.lat_caches, self.idx_caches, li.q_idx,
+        M.ml4_sparse_attn_layer(self.layers, l, self.seqs, self.lat_caches, self.idx_caches,
+                                li.q_idx,
                                 self.qi_dtype, li.q_idx_scale, li.w_idx, li.q_mla,
                                 self.qm_dtype, bufs, lens, self.out[l], self.qm_dtype,
                                 self.lse[l], self.ws, self.ws_bytes, self.fault, stream)

@@ -130,7 +130,7 @@ def test_e4m3_mla_default_deny():
     L.layer, L.kv_sharing_target_layer, L.topk_source_layer = 0, -1, -1
     L.rope_dim, L.top_k, L.idx_heads, L.mla_heads = 64, 2048, 64, 128
     L.softmax_scale = 0.04
-    rc = M.ml4_sparse_attn_layer(L, s, [_cache(M.ML4_LAT_E4M3_576)],
+    rc = M.ml4_sparse_attn_layer([L], 0, s, [_cache(M.ML4_LAT_E4M3_576)],
                                  [_cache(M.ML4_IDX_FP8_132)], 0x100, M.ML4_FP8_E4M3, None,
                                  0x100, 0x100, M.ML4_FP8_E4M3, [0x100], [0x100], 0x100,
                                  M.ML4_BF16, stream=0, check=False)
@@ -138,21 +138,54 @@ def test_e4m3_mla_default_deny():
     assert "ml4_sparse_mla_decode_e4m3" in M.ml4_last_error()
 
 
-def test_layer_modes_are_validated():
-    s = _seqs()
+def _layer(l, tgt=-1, src=-1, top_k=2048):
     L = M.ml4_layer()
-    L.layer, L.kv_sharing_target_layer, L.topk_source_layer = 1, 1, 2
-    L.rope_dim, L.top_k, L.idx_heads, L.mla_heads = 64, 2048, 64, 128
+    L.layer, L.kv_sharing_target_layer, L.topk_source_layer = l, tgt, src
+    L.rope_dim, L.top_k, L.idx_heads, L.mla_heads = 64, top_k, 64, 128
     L.softmax_scale = 0.04
-    caches = [_cache(M.ML4_LAT_FP8_656)] * 3
-    icaches = [_cache(M.ML4_IDX_FP8_132)] * 3
-    rc = M.ml4_sparse_attn_layer(L, s, caches, icaches, 0x100, M.ML4_FP8_E4M3, None, 0x100,
-                                 0x100, M.ML4_BF16, [0x100] * 3, [0x100] * 3, 0x100,
-                                 M.ML4_BF16, stream=0, check=False)
+    return L
+
+
+def _fused(layers, l, ws_bytes=0):
+    n = len(layers)
+    return M.ml4_sparse_attn_layer(layers, l, _seqs(), [_cache(M.ML4_LAT_FP8_656)] * n,
+                                   [_cache(M.ML4_IDX_FP8_132)] * n, 0x100, M.ML4_FP8_E4M3, None,
+                                   0x100, 0x100, M.ML4_BF16, [0x100] * n, [0x100] * n, 0x100,
+                                   M.ML4_BF16, stream=0, check=False, ws_bytes=ws_bytes)
+
+
+def test_layer_modes_are_validated():
+    rc = _fused([_layer(0), _layer(1, tgt=1, src=2), _layer(2)], 1)
     assert rc == M.ML4_E_INVALID
     msg = M.ml4_last_error()
     assert "kv_sharing_target_layer must be -1 or an earlier layer" in msg
     assert "topk_source_layer must be -1 or an earlier layer" in msg
+    rc = _fused([_layer(0), _layer(5)], 1)
+    assert rc == M.ML4_E_INVALID and "layers[layer].layer differs" in M.ml4_last_error()
+
+
+def test_layer_roles_no_chains_and_indexer_owner_sources():
+    """[blog, 跨层 KV 共享]: a consumer reads a layer that owns its cache, never another
+    consumer; a shared-indexer layer reuses the top-k of a layer that runs its own indexer,
+    with the same top_k (the shared rows' stride).  Each violation is listed; a valid
+    three-layer chain (owner, shared-indexer, consumer) passes validation up to the
+    workspace check (no workspace given, nothing launched)."""
+    layers = [_layer(0), _layer(1, tgt=0), _layer(2, tgt=1)]          # consumer of a consumer
+    assert _fused(layers, 2) == M.ML4_E_INVALID
+    assert "the target must own its cache" in M.ml4_last_error()
+    layers = [_layer(0), _layer(1, src=0), _layer(2, src=1)]          # sharer of a sharer
+    assert _fused(layers, 2) == M.ML4_E_INVALID
+    assert "the source must run its own indexer" in M.ml4_last_error()
+    layers = [_layer(0, top_k=1024), _layer(1, src=0, top_k=2048)]    # stride mismatch
+    assert _fused(layers, 1) == M.ML4_E_INVALID
+    assert "top_k differs from the topk_source_layer's top_k" in M.ml4_last_error()
+    layers = [_layer(0), _layer(1, tgt=0, src=0), _layer(2, tgt=1, src=1)]   # both at once
+    assert _fused(layers, 2) == M.ML4_E_INVALID
+    msg = M.ml4_last_error()
+    assert "the target must own its cache" in msg and "the source must run its own indexer" in msg
+    layers = [_layer(0), _layer(1, src=0), _layer(2, tgt=0)]          # the 1M-key three layers
+    for l in range(3):
+        assert _fused(layers, l) == M.ML4_E_WORKSPACE, M.ml4_last_error()
 
 
 def test_fault_query_rejects_null():
