@@ -22,7 +22,8 @@
  *     [blog, ROCm implementation details › Fail-stop: a sticky fault word checked after
  *     each forward] and the affected key or row is masked; kernels always run to
  *     completion.  ml4_fault_query() reads the word.
- *   - The library allocates no device memory and never calls hipMalloc/hipFree.
+ *   - The library allocates no device memory and never calls hipMalloc/hipFree; its only
+ *     device memory is the fixed scratch array of ml4_sparse_attn_layer_static.
  */
 #ifndef ML4DSA_H
 #define ML4DSA_H
@@ -271,6 +272,30 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
                           int32_t q_mla_dtype, int32_t* const* topk_bufs,
                           int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
                           void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream);
+
+/*
+ * ml4_sparse_attn_layer_static -- ml4_sparse_attn_layer without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It allocates nothing: the scratch (scores,
+ * top-k passes, split-MLA partials) is one fixed device array of ML4_STATIC_SCRATCH_BYTES
+ * inside the library, which each GPU the library runs on holds from the library's first
+ * use on it until the process ends.
+ *   Arguments, results, validation and fault bits as ml4_sparse_attn_layer.
+ *   A batch whose ml4_workspace_bytes(ML4_ENTRY_LAYER, ...) exceeds ML4_STATIC_SCRATCH_BYTES
+ *   is refused with ML4_E_UNSUPPORTED (nothing launched); 64 MiB holds the scores of
+ *   256 query rows at 65,536 positions or of one row at up to 16M positions.
+ *   Every call on one GPU uses that GPU's one array: calls that may overlap in time on the
+ *   same GPU (other streams, other host threads) race and must be ordered by the caller.
+ */
+#define ML4_STATIC_SCRATCH_BYTES (64u << 20)
+int ml4_sparse_attn_layer_static(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                                 const ml4_cache* lat_caches, const ml4_cache* idx_caches,
+                                 int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
+                                 const float* q_idx_scale, const float* w_idx,
+                                 const void* q_mla, int32_t q_mla_dtype,
+                                 int32_t* const* topk_bufs, int32_t* const* topk_lens,
+                                 void* out, int32_t out_dtype, float* lse, uint32_t* fault,
+                                 hipStream_t stream);
 
 /*
  * ml4_index_cache_write / ml4_latent_cache_write -- quantise and pack new tokens into the

@@ -180,6 +180,10 @@ void check_mla(Checks& c, const ml4_cache* kv, const void* q, int32_t q_dtype, i
 
 }  // namespace
 
+namespace ml4 {
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+}  // namespace ml4
+
 extern "C" {
 
 int ml4_abi_version(void) { return ML4_ABI_VERSION; }
@@ -368,13 +372,20 @@ int ml4_window_mla_decode(const ml4_seqs* s, const ml4_cache* kv, const void* q,
   return launch_status(ml4::launch_mla(a, stream), "ml4_window_mla_decode");
 }
 
-int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
-                          const ml4_cache* lat_caches, const ml4_cache* idx_caches,
-                          int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
-                          const float* q_idx_scale, const float* w_idx, const void* q_mla,
-                          int32_t q_mla_dtype, int32_t* const* topk_bufs,
-                          int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
-                          void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused layer.  static_scratch: the no-allocation form -- instead of the caller's
+// workspace, the library's fixed scratch array (its size checked here, its device address
+// looked up only after every check has passed).
+int fused_layer(const char* entry, const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                const ml4_cache* lat_caches, const ml4_cache* idx_caches, int32_t n_layers,
+                const void* q_idx, int32_t q_idx_dtype, const float* q_idx_scale,
+                const float* w_idx, const void* q_mla, int32_t q_mla_dtype,
+                int32_t* const* topk_bufs, int32_t* const* topk_lens, void* out,
+                int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, bool static_scratch,
+                uint32_t* fault, hipStream_t stream) {
   Checks c;
   check_seqs(c, s);
   c.bad(layers == nullptr, "layers is NULL");
@@ -383,7 +394,7 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
   c.bad(layer < 0 || layer >= n_layers, "layer outside 0 .. n_layers-1");
   if (!layers || n_layers < 1 || !lat_caches || !topk_bufs || !topk_lens || layer < 0 ||
       layer >= n_layers)
-    return c.finish("ml4_sparse_attn_layer");
+    return c.finish(entry);
   const ml4_layer* L = &layers[layer];
   const int l = layer;
   c.bad(L->layer != l, "layers[layer].layer differs from layer");
@@ -392,7 +403,7 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
   const bool src_ok = src == -1 || (src >= 0 && src < l);
   c.bad(!tgt_ok, "kv_sharing_target_layer must be -1 or an earlier layer");
   c.bad(!src_ok, "topk_source_layer must be -1 or an earlier layer");
-  if (!tgt_ok || !src_ok) return c.finish("ml4_sparse_attn_layer");
+  if (!tgt_ok || !src_ok) return c.finish(entry);
   // [blog, 跨层 KV 共享]: a consumer reads the cache of a layer that owns one (no chains);
   // [blog, Model architecture]: a shared-indexer layer reuses the top-k of a layer that runs
   // its own indexer, with the same top_k (the row stride of that layer's top-k buffer).
@@ -415,7 +426,6 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
         own_indexer ? "topk_bufs[layer] / topk_lens[layer] must be non-NULL"
                     : "topk_bufs[topk_source_layer] / topk_lens[topk_source_layer] must be non-NULL");
   const int64_t ld = s ? (int64_t)ml4::align_up((size_t)s->max_seq_len, 4) : 0;
-  float* scores = static_cast<float*>(ws);
   if (own_indexer) {
     c.bad(!idx_caches, "idx_caches is NULL for an indexer layer");
     if (idx_caches)
@@ -428,13 +438,28 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
   c.unsup(lat_caches[lat_layer].format == ML4_LAT_E4M3_576,
           "the fused layer takes ML4_LAT_FP8_656, ML4_LAT_BF16_1152 or ML4_LAT_F32 latent "
           "caches (ML4_LAT_E4M3_576: ml4_sparse_mla_decode_e4m3)");
-  size_t need = 0;
   if (c.invalid.empty() && c.unsupported.empty() && s) {
-    need = ml4_workspace_bytes(ML4_ENTRY_LAYER, s, L->mla_heads, L->top_k);
-    c.ws(ws_bytes < need, bytes_msg("layer workspace", need, ws_bytes));
-    c.ws(!ws || !aligned(ws, 256), "workspace must be non-NULL and 256-byte aligned");
+    const size_t need = ml4_workspace_bytes(ML4_ENTRY_LAYER, s, L->mla_heads, L->top_k);
+    if (static_scratch) {
+      c.unsupported.push_back(need > (size_t)ML4_STATIC_SCRATCH_BYTES
+                                  ? bytes_msg("this batch's scratch (above the fixed "
+                                              "ML4_STATIC_SCRATCH_BYTES; use "
+                                              "ml4_sparse_attn_layer with a workspace)",
+                                              need, (size_t)ML4_STATIC_SCRATCH_BYTES)
+                                  : std::string());
+      if (c.unsupported.back().empty()) c.unsupported.pop_back();
+    } else {
+      c.ws(ws_bytes < need, bytes_msg("layer workspace", need, ws_bytes));
+      c.ws(!ws || !aligned(ws, 256), "workspace must be non-NULL and 256-byte aligned");
+    }
   }
-  if (int rc = c.finish("ml4_sparse_attn_layer")) return rc;
+  if (int rc = c.finish(entry)) return rc;
+  if (static_scratch) {
+    const hipError_t e = ml4::static_scratch_address(&ws);
+    if (e != hipSuccess) return launch_status(e, entry);
+    ws_bytes = ML4_STATIC_SCRATCH_BYTES;
+  }
+  float* scores = static_cast<float*>(ws);
 
   const ml4::SeqView v = view(s);
   char* wsp = static_cast<char*>(ws);
@@ -456,7 +481,7 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
     ia.ld = ld;
     ia.fault = fault;
     e = ml4::launch_indexer(ia, stream);
-    if (e != hipSuccess) return launch_status(e, "ml4_sparse_attn_layer");
+    if (e != hipSuccess) return launch_status(e, entry);
     ml4::TopkLaunch ta{};
     ta.s = v;
     ta.scores = scores;
@@ -467,7 +492,7 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
     ta.ws = wsp + sc_bytes;
     ta.fault = fault;
     e = ml4::launch_topk(ta, stream);
-    if (e != hipSuccess) return launch_status(e, "ml4_sparse_attn_layer");
+    if (e != hipSuccess) return launch_status(e, entry);
   }
   ml4::MlaLaunch ma{};
   ma.s = v;
@@ -487,7 +512,37 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
   ma.lse = lse;
   ma.ws = wsp + sc_bytes + tk_bytes;
   ma.fault = fault;
-  return launch_status(ml4::launch_mla(ma, stream), "ml4_sparse_attn_layer");
+  return launch_status(ml4::launch_mla(ma, stream), entry);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                          const ml4_cache* lat_caches, const ml4_cache* idx_caches,
+                          int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
+                          const float* q_idx_scale, const float* w_idx, const void* q_mla,
+                          int32_t q_mla_dtype, int32_t* const* topk_bufs,
+                          int32_t* const* topk_lens, void* out, int32_t out_dtype, float* lse,
+                          void* ws, size_t ws_bytes, uint32_t* fault, hipStream_t stream) {
+  return fused_layer("ml4_sparse_attn_layer", layers, layer, s, lat_caches, idx_caches,
+                     n_layers, q_idx, q_idx_dtype, q_idx_scale, w_idx, q_mla, q_mla_dtype,
+                     topk_bufs, topk_lens, out, out_dtype, lse, ws, ws_bytes, false, fault,
+                     stream);
+}
+
+int ml4_sparse_attn_layer_static(const ml4_layer* layers, int32_t layer, const ml4_seqs* s,
+                                 const ml4_cache* lat_caches, const ml4_cache* idx_caches,
+                                 int32_t n_layers, const void* q_idx, int32_t q_idx_dtype,
+                                 const float* q_idx_scale, const float* w_idx,
+                                 const void* q_mla, int32_t q_mla_dtype,
+                                 int32_t* const* topk_bufs, int32_t* const* topk_lens,
+                                 void* out, int32_t out_dtype, float* lse, uint32_t* fault,
+                                 hipStream_t stream) {
+  return fused_layer("ml4_sparse_attn_layer_static", layers, layer, s, lat_caches, idx_caches,
+                     n_layers, q_idx, q_idx_dtype, q_idx_scale, w_idx, q_mla, q_mla_dtype,
+                     topk_bufs, topk_lens, out, out_dtype, lse, nullptr, 0, true, fault, stream);
 }
 
 namespace {

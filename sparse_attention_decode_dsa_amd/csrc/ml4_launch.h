@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace ml4 {
 
 struct SeqView {
@@ -114,5 +116,12 @@ struct LseCombineLaunch {
 hipError_t launch_lse_combine(const LseCombineLaunch& a, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Replaces the thread-local text that ml4_last_error() returns.
+void set_last_error(const std::string& msg);
+
+// Device address of the current device's copy of the library's fixed scratch array
+// (ML4_STATIC_SCRATCH_BYTES, 256-B aligned), looked up on its first use on that device.
+hipError_t static_scratch_address(void** out);
 
 }  // namespace ml4

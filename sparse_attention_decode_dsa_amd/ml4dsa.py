@@ -24,9 +24,11 @@ ML4_LAT_F32, ML4_LAT_FP8_656, ML4_LAT_BF16_1152, ML4_LAT_E4M3_576 = 0, 1, 2, 3
 ML4_FAULT_BLOCK_ID, ML4_FAULT_TOPK_INDEX, ML4_FAULT_NAN_SCORE, ML4_FAULT_QPOS = 1, 2, 4, 8
 ML4_FAULT_RANGE = 16
 ML4_ENTRY_TOPK, ML4_ENTRY_MLA, ML4_ENTRY_LAYER = 1, 2, 3
+ML4_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
-           "ml4_sparse_mla_decode_e4m3", "ml4_sparse_attn_layer", "ml4_window_mla_decode",
+           "ml4_sparse_mla_decode_e4m3", "ml4_sparse_attn_layer", "ml4_sparse_attn_layer_static",
+           "ml4_window_mla_decode",
            "ml4_index_cache_write", "ml4_latent_cache_write", "ml4_latent_cache_write_e4m3",
            "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
            "ml4_fault_query", "ml4_abi_version")
@@ -92,6 +94,10 @@ def _load() -> C.CDLL:
     lib.ml4_sparse_attn_layer.argtypes = [P(ml4_layer), i32, P(ml4_seqs), P(ml4_cache),
                                           P(ml4_cache), i32, vp, i32, vp, vp, vp, i32,
                                           P(vp), P(vp), vp, i32, vp, vp, sz, vp, vp]
+    lib.ml4_sparse_attn_layer_static.restype = C.c_int
+    lib.ml4_sparse_attn_layer_static.argtypes = [P(ml4_layer), i32, P(ml4_seqs), P(ml4_cache),
+                                                 P(ml4_cache), i32, vp, i32, vp, vp, vp, i32,
+                                                 P(vp), P(vp), vp, i32, vp, vp, vp]
     lib.ml4_index_cache_write.restype = C.c_int
     lib.ml4_index_cache_write.argtypes = [P(ml4_cache), i32, vp, i32, i64, vp, vp, vp]
     lib.ml4_latent_cache_write.restype = C.c_int
@@ -238,6 +244,26 @@ def ml4_sparse_attn_layer(layers: Sequence[ml4_layer], layer: int, seqs,
                                    q_idx_dtype, ptr(q_idx_scale), ptr(w_idx), ptr(q_mla),
                                    q_mla_dtype, bufs, lens, ptr(out), out_dtype, ptr(lse), ptr(ws),
                                    ws_bytes, ptr(fault), stream_handle(stream))
+    return _check(rc) if check else rc
+
+
+def ml4_sparse_attn_layer_static(layers: Sequence[ml4_layer], layer: int, seqs,
+                                 lat_caches: Sequence[ml4_cache],
+                                 idx_caches: Sequence[ml4_cache], q_idx, q_idx_dtype,
+                                 q_idx_scale, w_idx, q_mla, q_mla_dtype, topk_bufs, topk_lens,
+                                 out, out_dtype, lse=None, fault=None, stream=None,
+                                 check=True) -> int:
+    n = len(lat_caches)
+    descs = (ml4_layer * n)(*layers)
+    lat = (ml4_cache * n)(*lat_caches)
+    idx = (ml4_cache * n)(*idx_caches)
+    bufs = (C.c_void_p * n)(*[ptr(b) for b in topk_bufs])
+    lens = (C.c_void_p * n)(*[ptr(b) for b in topk_lens])
+    rc = LIB.ml4_sparse_attn_layer_static(descs, layer, C.byref(seqs), lat, idx, n, ptr(q_idx),
+                                          q_idx_dtype, ptr(q_idx_scale), ptr(w_idx),
+                                          ptr(q_mla), q_mla_dtype, bufs, lens, ptr(out),
+                                          out_dtype, ptr(lse), ptr(fault),
+                                          stream_handle(stream))
     return _check(rc) if check else rc
 
 

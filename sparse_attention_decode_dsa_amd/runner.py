@@ -121,6 +121,18 @@ class CaseRunner:
                                 self.qm_dtype, bufs, lens, self.out[l], self.qm_dtype,
                                 self.lse[l], self.ws, self.ws_bytes, self.fault, stream)
 
+    def run_layer_static(self, l: int, stream=None):
+        """The fused layer through the no-allocation entry (the library's fixed scratch
+        instead of this runner's workspace)."""
+        li = self.case.inputs[l]
+        bufs = [self.topk_idx.get(i) for i in range(self.n_layers)]
+        lens = [self.topk_len.get(i) for i in range(self.n_layers)]
+        M.ml4_sparse_attn_layer_static(self.layers, l, self.seqs, self.lat_caches,
+                                       self.idx_caches, li.q_idx, self.qi_dtype,
+                                       li.q_idx_scale, li.w_idx, li.q_mla, self.qm_dtype, bufs,
+                                       lens, self.out[l], self.qm_dtype, self.lse[l],
+                                       self.fault, stream)
+
     def run_layer_split(self, l: int, events: Optional[List] = None, stream=None):
         """indexer -> top-k -> MLA through the separate entries.  events, when given, is a
         list of 4 torch.cuda.Event recorded on the launch stream around the three calls."""

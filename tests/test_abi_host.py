@@ -188,6 +188,34 @@ def test_layer_roles_no_chains_and_indexer_owner_sources():
         assert _fused(layers, l) == M.ML4_E_WORKSPACE, M.ml4_last_error()
 
 
+def test_static_scratch_entry_validates_and_refuses_oversized_batches():
+    """The no-allocation fused entry runs the same default-deny checks (nothing launched, no
+    device touched when a check fails) and refuses a batch whose scratch exceeds the fixed
+    array, naming both sizes."""
+    text = open(HEADER).read()
+    assert re.search(r"#define ML4_STATIC_SCRATCH_BYTES \(64u << 20\)", text)
+    assert M.ML4_STATIC_SCRATCH_BYTES == 64 << 20
+    layers = [_layer(0)]
+    args = ([_cache(M.ML4_LAT_FP8_656)], [_cache(M.ML4_IDX_FP8_132)], 0x100, M.ML4_FP8_E4M3,
+            None, 0x100, 0x100, M.ML4_BF16, [0x100], [0x100], 0x100, M.ML4_BF16)
+    big = _seqs(total_q=512, max_q_per_seq=512, max_seq_len=65536, max_blocks_per_seq=1024)
+    rc = M.ml4_sparse_attn_layer_static(layers, 0, big, *args, stream=0, check=False)
+    msg = M.ml4_last_error()
+    assert rc == M.ML4_E_UNSUPPORTED and "ML4_STATIC_SCRATCH_BYTES" in msg
+    assert str(M.ml4_workspace_bytes(M.ML4_ENTRY_LAYER, big, 128, 2048)) in msg
+    assert str(64 << 20) in msg
+    bad = [_layer(0), _layer(1, tgt=0), _layer(2, tgt=1)]
+    rc = M.ml4_sparse_attn_layer_static(bad, 2, _seqs(block_size=48),
+                                        [_cache(M.ML4_LAT_FP8_656)] * 3,
+                                        [_cache(M.ML4_IDX_FP8_132)] * 3, 0x100, M.ML4_FP8_E4M3,
+                                        None, 0x100, 0x100, M.ML4_BF16, [0x100] * 3,
+                                        [0x100] * 3, 0x100, M.ML4_BF16, stream=0, check=False)
+    msg = M.ml4_last_error()
+    assert rc == M.ML4_E_INVALID
+    assert "the target must own its cache" in msg and "block_size must be a power of two" in msg
+    assert msg.startswith("ml4_sparse_attn_layer_static:")
+
+
 def test_fault_query_rejects_null():
     rc = M.LIB.ml4_fault_query(None, None, None)
     assert rc == M.ML4_E_INVALID
