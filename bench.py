@@ -7,7 +7,12 @@ SSMax s = 0.3; one RoPE layer and one NoPE layer per step.  Inputs are seeded sy
 data drawn on the GPU and resident in HBM before timing starts.
 
 One step = for each layer: indexer scores -> exact top-k -> sparse MLA (the three entry
-points the fused entry chains), timed with HIP events on the launch stream.
+points the fused entry chains), timed with HIP events on the launch stream.  Before each
+timed step a 1 GiB fill (outside the step's events) evicts the memory-side cache, so the
+decode workloads whose caches would fit in it still read them from HBM; value is query rows
+over the mean step time, with p10/p50/p90 and the back-to-back ("hot") time beside it.
+Each kernel is reported against its floors at datasheet peaks and against the rates a
+plain streaming read and a library GEMM reach on the same GPU.
 Prints one JSON line.  --gpus N > 1 is refused: the benchmark runs on one GPU.
 """
 
@@ -50,6 +55,8 @@ def parse():
                          "sliding-window attention")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the side measurement of the step captured into a HIP graph")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable streaming and GEMM rates")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused entry instead (no per-kernel events)")
     return ap.parse_args()
@@ -62,7 +69,9 @@ def kernel_hash(name: str) -> str:
 
 def algorithmic_work(case):
     """Per layer: indexer bytes (keys read once per request + queries), MLA bytes (selected
-    latent rows + q + o) and MLA FLOPs, from the workload's shape."""
+    latent rows + q + o) and MLA FLOPs, from the workload's shape.  The fp32 scores the
+    indexer writes and the selection reads back (4 B per visible position per row) are an
+    implementation overhead of the split path, reported apart as score_bytes."""
     b = case.batch
     seq = b.seq_lens.cpu().tolist()
     T, Hi, H = b.total_q, case.idx_heads, case.mla_heads
@@ -72,21 +81,20 @@ def algorithmic_work(case):
         k = d["top_k"]
         nsel = [min(k, p + 1) for p in qpos]
         idx_bytes = 0
+        score_bytes = 0
         if d["topk_source_layer"] < 0:
-            # cache rows read once per request, fp8 query + fp32 scale + weight per head,
-            # one fp32 score written per (row, position of its request)
-            rows_per_req = [b.q_start[i + 1].item() - b.q_start[i].item() for i in range(b.batch)]
-            idx_bytes = (sum(n * 132 for n in seq) + T * Hi * (128 + 8) +
-                         sum(q * n * 4 for q, n in zip(rows_per_req, seq)))
+            # cache rows read once per request, fp8 query + fp32 scale + weight per head
+            idx_bytes = sum(n * 132 for n in seq) + T * Hi * (128 + 8)
+            # one fp32 score per (row, visible position): written once, read by the top-k
+            score_bytes = sum(p + 1 for p in qpos) * 4
         rope = d["rope_dim"]
         row = 656 if rope else 528
         mla_bytes = sum(nsel) * row + T * H * (512 + rope) * 2 + T * H * 512 * 2
         mla_flops = sum(nsel) * 2 * H * (1024 + rope)
-        idx_flops = sum(n * 2 * Hi * 128 * q for n, q in
-                        zip(seq, [b.q_start[i + 1].item() - b.q_start[i].item()
-                                  for i in range(b.batch)])) if d["topk_source_layer"] < 0 else 0
+        # each row scores its visible positions 0 .. p (causal)
+        idx_flops = sum(p + 1 for p in qpos) * 2 * Hi * 128 if d["topk_source_layer"] < 0 else 0
         out[d["layer"]] = dict(idx_bytes=idx_bytes, idx_flops=idx_flops, mla_bytes=mla_bytes,
-                               mla_flops=mla_flops)
+                               mla_flops=mla_flops, score_bytes=score_bytes)
     return out
 
 
@@ -159,16 +167,23 @@ def cpu_baseline(case, budget_s: float):
     except Exception:
         cores = os.cpu_count()
     cpu_model = None
+    sockets, phys = set(), set()
     try:
         with open("/proc/cpuinfo") as f:
+            pid = None
             for line in f:
-                if line.startswith("model name"):
+                if line.startswith("model name") and cpu_model is None:
                     cpu_model = line.split(":", 1)[1].strip()
-                    break
+                elif line.startswith("physical id"):
+                    pid = line.split(":", 1)[1].strip()
+                    sockets.add(pid)
+                elif line.startswith("core id"):
+                    phys.add((pid, line.split(":", 1)[1].strip()))
     except OSError:
         pass
     return {"value": rows_done / elapsed, "unit": "query-tokens/s", "cores": cores,
-            "kind": "oracle", "cpu_model": cpu_model,
+            "kind": "oracle", "cpu_model": cpu_model, "nproc": os.cpu_count(),
+            "sockets": len(sockets) or None, "physical_cores": len(phys) or None,
             "sample": f"{rows_done} query rows ({len(sample)} whole requests), every layer of "
                       f"the step, fp64 numpy oracle; {elapsed:.1f} s of compute"}
 
@@ -323,6 +338,144 @@ def time_graph_step(run, K: int):
             "bit_identical_to_eager": bool(same), "steps": K}
 
 
+def achievable_peaks(dev: str):
+    """Rates a plain streaming read / copy and a vendor-library GEMM reach on this GPU:
+    the 'measured achievable' peaks each kernel is also compared against."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+    from sparse_attention_decode_dsa_amd import ml4dsa as M
+    out = {}
+    n = 1 << 31                                       # 2 GiB
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    sink = torch.zeros(8192, dtype=torch.float32, device=dev)
+    t = timed(lambda: M.ml4_probe_read(x, n, sink), 5)
+    out["hbm_read_GBps"] = n / t / 1e9               # the library's streaming-read probe
+    t = timed(lambda: y.copy_(x), 5)
+    out["hbm_copy_GBps"] = 2 * n / t / 1e9           # torch copy: read + write
+    del x, y
+    iters = 2000
+    nwave = 256 * 8 * 4 * 4
+    t = timed(lambda: M.ml4_probe_mfma(0, iters, sink), 3)
+    out["mfma_f16_TFLOPs"] = nwave * 16 * iters * 16384 / t / 1e12
+    t = timed(lambda: M.ml4_probe_mfma(1, iters // 2, sink), 3)
+    out["mfma_fp8_TFLOPs"] = nwave * 16 * (iters // 2) * 65536 / t / 1e12
+    m = 8192
+    for name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        a = torch.randn(m, m, device=dev).to(dt)
+        b = torch.randn(m, m, device=dev).to(dt)
+        t = timed(lambda: torch.matmul(a, b), 10)
+        out[f"gemm_{name}_TFLOPs"] = 2 * m ** 3 / t / 1e12
+        del a, b
+    try:
+        a = torch.randn(m, m, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn(m, m, device=dev).to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=dev)
+        t = timed(lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one,
+                                           out_dtype=torch.bfloat16), 10)
+        out["gemm_fp8_TFLOPs"] = 2 * m ** 3 / t / 1e12
+        del a, b
+    except Exception as e:            # not every torch build offers an fp8 GEMM here
+        out["gemm_fp8_TFLOPs"] = None
+        out["gemm_fp8_note"] = f"unavailable: {type(e).__name__}"
+    out["method"] = ("streaming-read probe over 2 GiB; torch copy_ of 2 GiB (read + "
+                     "write); MFMA probes: 16 independent chains per wave, 8 waves per SIMD; "
+                     "library GEMMs torch.matmul / _scaled_mm at 8192^3")
+    return out
+
+
+def kernel_report(work, per, layers, case, T, ach):
+    """Each kernel of each layer against its floors: HBM bytes at 8 TB/s, FP8 FLOPs at
+    5.0 and 16-bit FLOPs at 2.5 PFLOP/s (datasheet), and the same against the measured
+    achievable rates.  'binding' is the larger floor of the design the pages describe
+    (FP8 indexer, BF16 attention); 'impl' the larger floor of the arithmetic this library
+    uses (fp16 MFMA for both)."""
+    rep = {}
+    hbm_a = ach.get("hbm_read_GBps") or PEAK_HBM_GBS
+    f16_a = ach.get("mfma_f16_TFLOPs") or PEAK_F16_TFLOPS
+    fp8_a = ach.get("mfma_fp8_TFLOPs") or PEAK_FP8_TFLOPS
+    for l in layers:
+        w, pl = work[l], per[l]
+        ent = {}
+        for kern, us, nbytes, flops in (
+                ("indexer", pl["indexer_us"], w["idx_bytes"], w["idx_flops"]),
+                ("topk", pl["topk_us"], w["score_bytes"], 0),
+                ("mla", pl["mla_us"], w["mla_bytes"], w["mla_flops"])):
+            if us <= 0:
+                continue
+            hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e6
+            fp8 = flops / (PEAK_FP8_TFLOPS * 1e12) * 1e6
+            f16 = flops / (PEAK_F16_TFLOPS * 1e12) * 1e6
+            binding = max(hbm, fp8 if kern == "indexer" else f16)
+            impl = max(hbm, f16)
+            ach_floor = max(nbytes / (hbm_a * 1e9) * 1e6, flops / (f16_a * 1e12) * 1e6)
+            ent[kern] = {"us": us, "bytes": nbytes, "flops": flops,
+                         "floor_us": {"hbm": hbm, "fp8": fp8, "fp16": f16},
+                         "frac_binding": binding / us, "frac_impl": impl / us,
+                         "frac_achievable": ach_floor / us,
+                         "GBps": nbytes / (us * 1e-6) / 1e9,
+                         "TFLOPs": flops / (us * 1e-6) / 1e12}
+            if kern == "indexer" and flops:
+                ent[kern]["frac_fp8_achievable"] = flops / (fp8_a * 1e12) * 1e6 / us
+        rep[str(l)] = ent
+    return rep
+
+
+def time_mla_heads(case, run, dev: str, reps: int = 10):
+    """Sparse MLA of the workload's first layer at 64 and 16 query heads (the pages' model
+    has 64; a four-way tensor-parallel share is 16) on the same selections: the regime where
+    the gather of 656-byte rows, not the matrix cores, bounds the kernel."""
+    import torch
+
+    from sparse_attention_decode_dsa_amd import ml4dsa as M
+    d = case.layers[0]
+    l = d["layer"]
+    b = case.batch
+    rope, K = d["rope_dim"], d["top_k"]
+    li = case.inputs[l]
+    idx, ln = run.topk_of(l)
+    nsel = int(ln.clamp(min=0).sum().item())
+    fault = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    for H in (64, 16):
+        q = li.q_mla[:, :H].contiguous()
+        out = torch.empty((b.total_q, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((b.total_q, H), dtype=torch.float32, device=dev)
+        wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_MLA, run.seqs, H, K)
+        ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=dev)
+        fn = lambda: M.ml4_sparse_mla_decode(run.seqs, run.lat_pool_of(l), q, M.ML4_BF16, H,
+                                             rope, idx, ln, K, d["softmax_scale"],
+                                             d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault)
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        row = 656 if rope else 528
+        nbytes = nsel * row + b.total_q * H * ((512 + rope) * 2 + 512 * 2)
+        flops = 2.0 * H * (1024 + rope) * nsel
+        res[f"heads_{H}"] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                             "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                             "TFLOPs": flops / (us * 1e-6) / 1e12,
+                             "frac_f16_peak": flops / (us * 1e-6) / 1e12 / PEAK_F16_TFLOPS}
+    assert M.ml4_fault_query(fault) == 0
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,24 +503,40 @@ def main():
     assert run.fault_bits() == 0, "fault word set during warm-up"
 
     K = args.steps
+    # Timed region: K steps.  Before each step, outside its events, a 1 GiB fill evicts the
+    # 256 MB memory-side cache (MALL) and the L2s, so every step reads its caches from HBM
+    # (the small decode workloads would otherwise fit in the MALL).  Each step is bracketed
+    # by its own events; per-kernel events sit on the launch stream inside the step.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     ev = {l: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
           for l in layers}
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
     for k in range(K):
+        flush.fill_(k & 0xFF)
+        sev[k][0].record()
         for l in layers:
             if args.fused:
                 run.run_layer_fused(l)
             else:
                 run.run_layer_split(l, events=ev[l][k])
-    stop.record()
+        sev[k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / K
+    step_ms = sorted(sev[k][0].elapsed_time(sev[k][1]) for k in range(K))
+    ms = sum(step_ms) / K
+    pct = lambda q: step_ms[min(K - 1, int(round(q * (K - 1))))]
     assert run.fault_bits() == 0, "fault word set during timing"
+    # The same steps back to back, no eviction in between (caches warm where they fit).
+    hot = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    hot[0].record()
+    for k in range(K):
+        run.run_step(fused=args.fused)
+    hot[1].record()
+    torch.cuda.synchronize()
+    hot_ms = hot[0].elapsed_time(hot[1]) / K
+    del flush
 
     work = algorithmic_work(case)
     T = case.batch.total_q
@@ -382,6 +551,7 @@ def main():
                 "mla_us": 1e3 * sum(ev[l][k][2].elapsed_time(ev[l][k][3]) for k in range(K)) / K,
             }
     step_bytes = sum(w["idx_bytes"] + w["mla_bytes"] for w in work.values())
+    score_bytes = sum(w["score_bytes"] for w in work.values())
     result = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -405,7 +575,13 @@ def main():
                                                 "topk_source_layer", "ssmax_s")}
                             for d in case.layers],
             "us_per_layer_step": 1e3 * ms / len(layers),
+            "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "timing": "each step after a 1 GiB fill that evicts MALL/L2, outside its events; "
+                      "value = query rows / mean step time",
+            "hot_ms_per_step": hot_ms,
+            "algorithmic_bytes_per_step": step_bytes,
             "algorithmic_GBps": step_bytes / (ms * 1e-3) / 1e9,
+            "score_roundtrip_bytes_per_step": score_bytes,
             "per_layer_us": per,
             "wall_s": wall,
         },
@@ -427,7 +603,7 @@ def main():
             nbytes, flops = work[l0]["mla_bytes"], work[l0]["mla_flops"]
         else:
             us = per[l0]["topk_us"]
-            nbytes, flops = T * case.batch.max_seq_len * 4, 0
+            nbytes, flops = work[l0]["score_bytes"], 0
         t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
         t_mfma = flops / (PEAK_F16_TFLOPS * 1e12)
         if t_mfma > t_hbm:
@@ -455,6 +631,13 @@ def main():
         assert run.fault_bits() == 0, "fault word set during the graph measurement"
     if not args.no_layouts and case.fmt == "fp8":
         result["layouts"] = time_layouts(case, run, dev)
+        result["mla_heads"] = time_mla_heads(case, run, dev)
+    if not args.no_peaks:
+        print("[bench] measuring achievable peaks", file=sys.stderr, flush=True)
+        result["achievable_peaks"] = achievable_peaks(dev)
+        if per:
+            result["kernels"] = kernel_report(work, per, layers, case, T,
+                                              result["achievable_peaks"])
     if args.cache_write_tokens > 0:
         result["cache_write"] = time_cache_writes(args.cache_write_tokens, dev)
     if args.cpu_seconds > 0:

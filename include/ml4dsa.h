@@ -379,6 +379,19 @@ int ml4_lse_combine(int32_t rows, int32_t n_heads, int32_t n_shards, int32_t hea
                     const float* o_parts, const float* lse_parts, void* out, int32_t out_dtype,
                     float* lse, hipStream_t stream);
 
+/*
+ * Measurement probes (not part of the attention path): the rates a plain streaming read
+ * and back-to-back independent MFMAs reach on this GPU, against which the kernels above
+ * are also measured.  ml4_probe_read reads `bytes` (a multiple of 16, 16-B aligned) of
+ * `buf` once; ml4_probe_mfma runs 256 * 8 * 4 work-groups of 4 waves, each wave issuing
+ * 16 * iters MFMAs: kind 0 = v_mfma_f32_16x16x32_f16 (16,384 FLOP each), kind 1 =
+ * v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3 (65,536 FLOP each).  `sink` is a device buffer
+ * of at least 8192 floats the kernels may write.  Return 0, -1 (invalid argument) or -4
+ * (launch refused); asynchronous on `stream`.
+ */
+int ml4_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+int ml4_probe_mfma(int32_t kind, int32_t iters, float* sink, hipStream_t stream);
+
 enum ml4_entry { ML4_ENTRY_TOPK = 1, ML4_ENTRY_MLA = 2, ML4_ENTRY_LAYER = 3 };
 
 /* Workspace bytes an entry point needs for this batch (256-B aligned start required).

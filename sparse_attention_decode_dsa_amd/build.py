@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libml4dsa.so")
 SOURCES = ["abi.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_write.hip",
-           "merge.hip", "static_ws.hip"]
+           "merge.hip", "static_ws.hip", "probe.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code.

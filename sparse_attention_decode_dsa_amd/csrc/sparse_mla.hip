@@ -405,7 +405,10 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int tid = threadIdx.x, tid0 = tid;
   const int lane0 = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int hg = wave & 3, dh = wave >> 2;
+  // Partners (same heads, other latent half) are waves 2 hg and 2 hg + 1; with fewer than
+  // 128 heads the idle head groups are the high ones, so the active waves spread over the
+  // four SIMDs (wave w runs on SIMD w % 4).
+  const int hg = wave >> 1, dh = wave & 1;
   const int r = blockIdx.x;
   const int hbase = blockIdx.y * kHeadsPerWg;
   const int h0 = hbase + hg * 32;
@@ -585,8 +588,9 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     f32x4* xsb = xs + (G::ONEBAR ? (tile & 1) * G::XS_WORDS : 0);
 
     // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
-    //      partner waves then add half 0 + half 1 in the same order
-    {
+    //      partner waves then add half 0 + half 1 in the same order.  Waves whose heads are
+    //      all past n_heads only move data and keep the barriers.
+    if (active) {
       const __bf16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
       f32x4* mine = xsb + wave * 4 * kWave;
 #pragma unroll
@@ -608,10 +612,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     } else {
       __syncthreads();
     }
+    if (!active) continue;
     float pv[2][2][4];
     {
-      const f32x4* p0 = xsb + hg * 4 * kWave;
-      const f32x4* p1 = xsb + (hg | 4) * 4 * kWave;
+      const f32x4* p0 = xsb + (2 * hg) * 4 * kWave;
+      const f32x4* p1 = xsb + (2 * hg + 1) * 4 * kWave;
       // slots of accumulator keys (kt, 4 g + j): selection index 8 g + 2 j + kt with the
       // interleaved rows of fp8_ds_mla tiles, 16 kt + 4 g + j otherwise
       constexpr bool IL = FMT == kFmtFp8;

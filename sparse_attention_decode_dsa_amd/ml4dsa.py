@@ -31,7 +31,7 @@ EXPORTS = ("ml4_indexer_score", "ml4_topk_select", "ml4_sparse_mla_decode",
            "ml4_window_mla_decode",
            "ml4_index_cache_write", "ml4_latent_cache_write", "ml4_latent_cache_write_e4m3",
            "ml4_topk_merge", "ml4_lse_combine", "ml4_workspace_bytes", "ml4_last_error",
-           "ml4_fault_query", "ml4_abi_version")
+           "ml4_fault_query", "ml4_abi_version", "ml4_probe_read", "ml4_probe_mfma")
 
 
 class ml4_seqs(C.Structure):
@@ -113,6 +113,10 @@ def _load() -> C.CDLL:
     lib.ml4_topk_merge.argtypes = [i32, i32, vp, vp, vp, i64, i32, vp, vp, vp, vp]
     lib.ml4_lse_combine.restype = C.c_int
     lib.ml4_lse_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.ml4_probe_read.restype = C.c_int
+    lib.ml4_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.ml4_probe_mfma.restype = C.c_int
+    lib.ml4_probe_mfma.argtypes = [i32, i32, vp, vp]
     if lib.ml4_abi_version() != ML4_ABI_VERSION:
         raise ImportError("libml4dsa.so ABI version mismatch")
     return lib
@@ -315,3 +319,11 @@ def ml4_window_mla_decode(seqs, kv, q, q_dtype, n_heads, rope_dim, window, softm
                                    out_dtype, ptr(lse), ptr(ws), ws_bytes, ptr(fault),
                                    stream_handle(stream))
     return _check(rc) if check else rc
+
+
+def ml4_probe_read(buf, nbytes, sink, stream=None) -> int:
+    return LIB.ml4_probe_read(ptr(buf), nbytes, ptr(sink), stream_handle(stream))
+
+
+def ml4_probe_mfma(kind, iters, sink, stream=None) -> int:
+    return LIB.ml4_probe_mfma(kind, iters, ptr(sink), stream_handle(stream))
