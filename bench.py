@@ -8,9 +8,11 @@ data drawn on the GPU and resident in HBM before timing starts.
 
 One step = for each layer: indexer scores -> exact top-k -> sparse MLA (the three entry
 points the fused entry chains), timed with HIP events on the launch stream.  Before each
-timed step a 1 GiB fill (outside the step's events) evicts the memory-side cache, so the
-decode workloads whose caches would fit in it still read them from HBM; value is query rows
-over the mean step time, with p10/p50/p90 and the back-to-back ("hot") time beside it.
+timed step a streaming read of an unrelated 1 GiB buffer (outside the step's events) evicts
+the memory-side cache and the L2s with clean lines, so the decode workloads whose caches
+would fit in the 256 MB memory-side cache still read them from HBM, and no step pays for
+write-backs of data it did not write; value is query rows over the mean step time, with
+p10/p50/p90 and the back-to-back ("hot") time beside it.
 Each kernel is reported against its floors at datasheet peaks and against the rates a
 plain streaming read and a library GEMM reach on the same GPU.
 Prints one JSON line.  --gpus N > 1 is refused: the benchmark runs on one GPU.
@@ -446,6 +448,8 @@ def time_mla_heads(case, run, dev: str, reps: int = 10):
     idx, ln = run.topk_of(l)
     nsel = int(ln.clamp(min=0).sum().item())
     fault = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros(8192, dtype=torch.float32, device=dev)
     res = {}
     for H in (64, 16):
         q = li.q_mla[:, :H].contiguous()
@@ -458,13 +462,15 @@ def time_mla_heads(case, run, dev: str, reps: int = 10):
                                              d["ssmax_s"], out, M.ML4_BF16, lse, ws, wsn, fault)
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in evs:       # each call after the same clean 1 GiB eviction as the steps
+            if M.ml4_probe_read(flush, flush.numel() * 4, flush_sink) != 0:
+                raise RuntimeError(M.ml4_last_error())
+            e[0].record()
             fn()
-        e1.record()
+            e[1].record()
         torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / reps
+        us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in evs) / reps
         row = 656 if rope else 528
         nbytes = nsel * row + b.total_q * H * ((512 + rope) * 2 + 512 * 2)
         flops = 2.0 * H * (1024 + rope) * nsel
@@ -503,18 +509,25 @@ def main():
     assert run.fault_bits() == 0, "fault word set during warm-up"
 
     K = args.steps
-    # Timed region: K steps.  Before each step, outside its events, a 1 GiB fill evicts the
-    # 256 MB memory-side cache (MALL) and the L2s, so every step reads its caches from HBM
-    # (the small decode workloads would otherwise fit in the MALL).  Each step is bracketed
-    # by its own events; per-kernel events sit on the launch stream inside the step.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Timed region: K steps.  Before each step, outside its events, a streaming read of a
+    # 1 GiB buffer (written once, here) evicts the 256 MB memory-side cache (MALL) and the
+    # L2s, so every step reads its caches from HBM (the small decode workloads would
+    # otherwise fit in the MALL).  The eviction is a read, not a fill: a fill leaves the
+    # caches full of dirty lines whose write-back then competes with the step's own reads
+    # (measured: a 138 MB read after a 1 GiB fill runs at 2.3 TB/s, after a 1 GiB read at
+    # 4.8 TB/s).  Each step is bracketed by its own events; per-kernel events sit on the
+    # launch stream inside the step.
+    from sparse_attention_decode_dsa_amd import ml4dsa as M
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros(8192, dtype=torch.float32, device=dev)
     ev = {l: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
           for l in layers}
     sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        flush.fill_(k & 0xFF)
+        if M.ml4_probe_read(flush, flush.numel() * 4, flush_sink) != 0:
+            raise RuntimeError(M.ml4_last_error())
         sev[k][0].record()
         for l in layers:
             if args.fused:
@@ -536,7 +549,7 @@ def main():
     hot[1].record()
     torch.cuda.synchronize()
     hot_ms = hot[0].elapsed_time(hot[1]) / K
-    del flush
+    del flush, flush_sink
 
     work = algorithmic_work(case)
     T = case.batch.total_q
@@ -576,7 +589,8 @@ def main():
                             for d in case.layers],
             "us_per_layer_step": 1e3 * ms / len(layers),
             "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-            "timing": "each step after a 1 GiB fill that evicts MALL/L2, outside its events; "
+            "timing": "each step after a 1 GiB streaming read that evicts MALL/L2 with clean lines, "
+                      "outside its events; "
                       "value = query rows / mean step time",
             "hot_ms_per_step": hot_ms,
             "algorithmic_bytes_per_step": step_bytes,

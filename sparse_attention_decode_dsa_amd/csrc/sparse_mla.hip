@@ -139,7 +139,7 @@ static_assert(MlaGeom<64, kFmtE4m3>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<0, kFmtE4m3>::RS == 528 && MlaGeom<64, kFmtE4m3>::RS == 576, "rows");
 
 // Work split inside a work-group of 8 waves (one query row, up to 128 heads): wave w owns
-// head group hg = w & 3 (32 heads = two 16-head MFMA tiles) and dim half dh = w >> 2
+// head group hg = w >> 1 (32 heads = two 16-head MFMA tiles) and dim half dh = w & 1
 // (latent dims 256 dh .. 256 dh + 255, RoPE dims 32 dh .. 32 dh + 31).  Every K or V
 // fragment read from LDS feeds two MFMAs.  Per wave the latent query takes 64 registers and
 // the output accumulator 128; the RoPE query is read from LDS per tile.

@@ -15,7 +15,9 @@
 //      are kept lowest-t first until k are chosen (wave ballots + block prefix sums).
 // Rows up to 131,072 positions first narrow the row to an LDS candidate list with a
 // threshold taken from a sample (one read of the row), and run steps 2-3 on that list; the
-// streaming form above is their fallback when the list misses.  Longer rows use a
+// streaming form above is their fallback when the list misses.  Rows up to 32,768 positions
+// hold the whole row in registers (32 keys per thread), so the sample and the candidate
+// pass read no memory.  Longer rows use a
 // multi-work-group version with the same steps, one launch per pass over the row, its
 // histograms merged with integer atomics; each work-group of a pass redoes the per-row
 // digit pick from the previous pass's histogram, so no launch is spent on it.
@@ -386,6 +388,67 @@ __device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above
   return shift > 0 ? P << shift : P;
 }
 
+// Step 3 of the candidate filter, shared by the one-row kernels: the K-th key of the LDS list
+// cand_key/cand_t[0 .. m) (m >= K, every key outside the list below it), then the kept
+// positions in ascending order through position bitmaps of WPT words per thread.  Every
+// thread of the work-group must call it.
+template <int WPT>
+__device__ void finish_from_candidates(const TopkLaunch& a, int r, int n, const uint32_t* cand_key,
+                                       const int* cand_t, int m, uint32_t* sel_bits,
+                                       uint32_t* tie_bits, uint32_t* hist, int* sh_scan,
+                                       int* sh_sel) {
+  const int K = a.top_k;
+  const int tid = threadIdx.x;
+  int above;
+  const uint32_t kth = lds_select(cand_key, m, K, &above, hist, sh_scan, sh_sel);
+  const int need_eq = K - above;          // keys equal to kth to keep, lowest position first
+  const int nw = (n + 31) >> 5;
+  for (int i = tid; i < nw; i += kRowThreads) { sel_bits[i] = 0u; tie_bits[i] = 0u; }
+  __syncthreads();
+  for (int i = tid; i < m; i += kRowThreads) {
+    const uint32_t k = cand_key[i];
+    const int t = cand_t[i];
+    if (k > kth) atomicOr(&sel_bits[t >> 5], 1u << (t & 31));
+    else if (k == kth) atomicOr(&tie_bits[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  // thread tid owns words [WPT * tid, WPT * tid + WPT)
+  const int w0 = WPT * tid;
+  int my_ties = 0;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) my_ties += (w0 + q < nw) ? __builtin_popcount(tie_bits[w0 + q]) : 0;
+  int tot;
+  int tie_rank = block_exclusive_scan<kRowThreads>(my_ties, &tot, sh_scan);
+  uint32_t keep[WPT];
+  int my_sel = 0;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    uint32_t sb = (w0 + q < nw) ? sel_bits[w0 + q] : 0u;
+    uint32_t tb = (w0 + q < nw) ? tie_bits[w0 + q] : 0u;
+    while (tb) {                                 // ties in ascending position
+      const uint32_t low = tb & (0u - tb);
+      if (tie_rank < need_eq) sb |= low;
+      ++tie_rank;
+      tb ^= low;
+    }
+    keep[q] = sb;
+    my_sel += __builtin_popcount(sb);
+  }
+  int at = block_exclusive_scan<kRowThreads>(my_sel, &tot, sh_scan);
+  int32_t* out = a.idx + (size_t)r * K;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    uint32_t sb = keep[q];
+    while (sb) {
+      const int bit = __builtin_ctz(sb);
+      if (at < K) out[at] = 32 * (w0 + q) + bit;
+      ++at;
+      sb &= sb - 1;
+    }
+  }
+  if (tid == 0) a.len[r] = K;
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
   constexpr int NW = kRowThreads / kWave;
   __shared__ uint32_t cand_key[kCand];
@@ -501,55 +564,119 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
   }
 
   // 3. K-th key of the list, then the kept positions in ascending order
-  int above;
-  const uint32_t kth = lds_select(cand_key, m, K, &above, hist, sh_scan, sh_sel);
-  const int need_eq = K - above;          // keys equal to kth to keep, lowest position first
-  const int nw = (n + 31) >> 5;
-  for (int i = tid; i < nw; i += kRowThreads) { sel_bits[i] = 0u; tie_bits[i] = 0u; }
-  __syncthreads();
-  for (int i = tid; i < m; i += kRowThreads) {
-    const uint32_t k = cand_key[i];
-    const int t = cand_t[i];
-    if (k > kth) atomicOr(&sel_bits[t >> 5], 1u << (t & 31));
-    else if (k == kth) atomicOr(&tie_bits[t >> 5], 1u << (t & 31));
+  finish_from_candidates<kMaxCandRow / 32 / kRowThreads>(a, r, n, cand_key, cand_t, m, sel_bits,
+                                                         tie_bits, hist, sh_scan, sh_sel);
+}
+
+
+// ------------------------------------------------------- whole row in registers, one row per WG
+// Rows up to 4,096 V positions: thread tid holds the row's float4 vectors tid + 1,024 j,
+// j < V, as order-preserving keys, all loaded in one go.  The steps are those of the
+// candidate filter above, but the sample and the candidate pass read these registers
+// instead of the row, so the row is read from memory once and the sample selection
+// overlaps the tail of its transfer.  The sample: each thread's vector tid % V (4,096 keys
+// spread over the row).  A list that misses (fewer than K keys or more than kCandReg) falls
+// back to the streaming exact selection.
+constexpr int kCandReg = 4096;
+
+template <int V>
+__global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
+  constexpr int NW = kRowThreads / kWave;
+  constexpr int WPT = V >= 8 ? V / 8 : 1;        // bitmap words per thread (n / 32 words)
+  __shared__ uint32_t cand_key[kCandReg];
+  __shared__ int cand_t[kCandReg];
+  __shared__ uint32_t sel_bits[WPT * kRowThreads], tie_bits[WPT * kRowThreads];
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ int sh_scan[NW];
+  __shared__ int sh_sel[4];
+  __shared__ int sh_count, sh_nan;
+
+  const int r = blockIdx.x;
+  int n = 0;
+  if (!row_prologue(a, r, &n)) return;
+  const int K = a.top_k;
+  const float* row = a.scores + (size_t)r * a.ld;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int n4 = (n + 3) >> 2;
+  if (tid == 0) { sh_count = 0; sh_nan = 0; }
+
+  // Key 0 (below every order key of a number) marks NaN and the positions past n; the
+  // threshold is at least 1, so they never enter the list, and a row with fewer than K other
+  // keys misses and takes the exact path, which ranks NaN below -inf.
+  uint32_t key[V][4];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i4 = tid + kRowThreads * j;
+    const u32x4 x = i4 < n4 ? *reinterpret_cast<const u32x4*>(row + 4 * i4) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[j][e] = x[e];
   }
-  __syncthreads();
-  // thread tid owns words [wpt * tid, wpt * tid + wpt)
-  constexpr int kWpt = kMaxCandRow / 32 / kRowThreads;   // 4
-  const int w0 = kWpt * tid;
-  int my_ties = 0;
+  bool any_nan = false;
 #pragma unroll
-  for (int q = 0; q < kWpt; ++q) my_ties += (w0 + q < nw) ? __builtin_popcount(tie_bits[w0 + q]) : 0;
-  int tot;
-  int tie_rank = block_exclusive_scan<kRowThreads>(my_ties, &tot, sh_scan);
-  uint32_t keep[kWpt];
-  int my_sel = 0;
+  for (int j = 0; j < V; ++j)
 #pragma unroll
-  for (int q = 0; q < kWpt; ++q) {
-    uint32_t sb = (w0 + q < nw) ? sel_bits[w0 + q] : 0u;
-    uint32_t tb = (w0 + q < nw) ? tie_bits[w0 + q] : 0u;
-    while (tb) {                                 // ties in ascending position
-      const uint32_t low = tb & (0u - tb);
-      if (tie_rank < need_eq) sb |= low;
-      ++tie_rank;
-      tb ^= low;
+    for (int e = 0; e < 4; ++e) {
+      bool nn = false;
+      const uint32_t k = order_key(__uint_as_float(key[j][e]), nn);
+      const bool valid = 4 * (tid + kRowThreads * j) + e < n;
+      key[j][e] = valid ? k : 0u;
+      any_nan |= nn && valid;
     }
-    keep[q] = sb;
-    my_sel += __builtin_popcount(sb);
-  }
-  int at = block_exclusive_scan<kRowThreads>(my_sel, &tot, sh_scan);
-  int32_t* out = a.idx + (size_t)r * K;
+
+  // 1. threshold (22 leading bits are enough; the low 10 are left clear)
+  uint32_t T = 1u;
+  if (n > kCandReg) {
+    // n > 4,096: every thread's vector 0 is inside the row
+    int js = tid % V;
+    while (js > 0 && tid + kRowThreads * js >= n4) --js;
+    uint32_t sk[4] = {key[0][0], key[0][1], key[0][2], key[0][3]};
 #pragma unroll
-  for (int q = 0; q < kWpt; ++q) {
-    uint32_t sb = keep[q];
-    while (sb) {
-      const int bit = __builtin_ctz(sb);
-      if (at < K) out[at] = 32 * (w0 + q) + bit;
-      ++at;
-      sb &= sb - 1;
-    }
+    for (int j = 1; j < V; ++j)
+      if (j == js) { sk[0] = key[j][0]; sk[1] = key[j][1]; sk[2] = key[j][2]; sk[3] = key[j][3]; }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cand_key[4 * tid + e] = sk[e];
+    __syncthreads();
+    const int ns = 4 * kRowThreads;
+    const int rank = min(ns, (int)(1.5f * (float)K * (float)ns / (float)n) + 8);
+    int above;
+    T = max(1u, lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel, 10));
   }
-  if (tid == 0) a.len[r] = K;
+  __syncthreads();
+
+  // 2. candidate list from the registers
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += key[j][e] >= T ? 1 : 0;
+  const int incl = wave_incl_scan(c);
+  int slot = 0;
+  if (lane == kWave - 1) slot = atomicAdd(&sh_count, incl);
+  slot = __shfl(slot, kWave - 1) + incl - c;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (key[j][e] >= T) {
+        if (slot < kCandReg) {
+          cand_key[slot] = key[j][e];
+          cand_t[slot] = 4 * (tid + kRowThreads * j) + e;
+        }
+        ++slot;
+      }
+  if (any_nan) sh_nan = 1;
+  __syncthreads();
+  const int m = sh_count;
+  if (tid == 0 && sh_nan) raise_fault(a.fault, kFaultNan);
+  if (m < K || m > kCandReg) {    // threshold missed: exact selection over the whole row
+    __syncthreads();
+    row_select_exact<false>(a, r, n, nullptr);
+    return;
+  }
+  // 3. K-th key of the list, then the kept positions in ascending order
+  finish_from_candidates<WPT>(a, r, n, cand_key, cand_t, m, sel_bits, tie_bits, hist, sh_scan,
+                              sh_sel);
 }
 
 // ------------------------------------------------------------------ many work-groups per row
@@ -902,6 +1029,13 @@ size_t topk_ws_bytes(const SeqView& s, int top_k) {
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   const SeqView& s = a.s;
+  if (s.max_seq_len <= 4 * kRowThreads * 8) {
+    if (s.max_seq_len <= 4 * kRowThreads * 4)
+      k_topk_reg<4><<<s.total_q, kRowThreads, 0, st>>>(a);
+    else
+      k_topk_reg<8><<<s.total_q, kRowThreads, 0, st>>>(a);
+    return hipGetLastError();
+  }
   if (s.max_seq_len <= kMaxCandRow) {
     k_topk_cand<<<s.total_q, kRowThreads, 0, st>>>(a);
     return hipGetLastError();

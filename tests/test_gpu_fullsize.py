@@ -1,7 +1,10 @@
 """Parity at the five workloads' full sizes, on the inputs and through the entries the bench
 times (MI355X only): the seeded workload is generated on the GPU exactly as the bench does
 and each layer runs through the separate entries with the bench's launch configuration.
-On sampled query rows (first, middle, last) the oracle recomputes, one row at a time:
+On sampled query rows the oracle recomputes, one row at a time.  The sample holds every row
+of a small batch, else whole groups of four consecutive rows (the first, a middle and the
+last group: every slot of a multi-row indexer work-group) and, for long prefill rows, 16
+rows spread evenly over the causal range (so over several key chunks):
 
 * indexer scores over every visible key, within 2e-5 of the row's largest |score| (fp32
   accumulation of exact e4m3 products), -inf past the row's position;
@@ -10,7 +13,10 @@ On sampled query rows (first, middle, last) the oracle recomputes, one row at a 
   fp64 scores up to near-ties (tests/compare.py);
 * attention output and LSE, |d| <= 2e-3 + 1e-2 |ref|, with the layer modes resolved as the
   bench runs them (shared-indexer layers reuse the owner's top-k, consumers read the
-  owner's latent cache).
+  owner's latent cache);
+* end to end: attention on the oracle's own top-k set (from its fp64 scores) against the
+  GPU output, reported per layer; where the two sets are equal it must meet the attention
+  bound as well.
 """
 
 import numpy as np
@@ -41,7 +47,13 @@ def _say(msg):
 
 
 def _sample_rows(total_q):
-    return sorted({0, total_q // 2, total_q - 1})
+    if total_q <= 8:
+        return list(range(total_q))
+    mid = (total_q // 2) & ~3
+    rows = set(range(4)) | set(range(mid, mid + 4)) | set(range(total_q - 4, total_q))
+    if total_q >= 1024:
+        rows |= {int(round(x)) for x in np.linspace(0, total_q - 1, 16)}
+    return sorted(rows)
 
 
 @pytest.mark.parametrize("config", [2, 3, 4, 5])
@@ -53,7 +65,7 @@ def test_full_size_workload_sampled_rows(config):
     rows = _sample_rows(s.total_q)
     _say(f"[gpu] full-size {case.name}: rows {s.total_q}, context {case.batch.max_seq_len}, "
          f"sampled rows {rows}")
-    lat_np = {}
+    lat_np, own_sets = {}, {}
     for d in case.layers:
         l = d["layer"]
         li = case.inputs[l]
@@ -76,17 +88,39 @@ def test_full_size_workload_sampled_rows(config):
                 assert np.array_equal(gi_all[r], oi), f"layer {l} row {r}: top-k differs"
             ties, log = check_topk_rows(gi_all, gl_all, ref, s.q_pos, d["top_k"], rows)
             _say(f"  layer {l}: scores and top-k ok (fp64 near-ties {ties})")
+            own_sets[l] = [O.topk_row(ref[i], int(s.q_pos[r]), d["top_k"]) for i, r in
+                           enumerate(rows)]
         idx, ln = run.topk_of(l)
         gi, gl = t_np(idx), t_np(ln)
         lat_l = d["kv_sharing_target_layer"] if d["kv_sharing_target_layer"] >= 0 else l
         if lat_l not in lat_np:
             lat_np[lat_l] = t_np(case.inputs[lat_l].lat_pool)
-        o, lse = O.sparse_mla(s, lat_np[lat_l], case.fmt, t_np(li.q_mla), d["rope_dim"], gi, gl,
+        q_bits = t_np(li.q_mla)
+        o, lse = O.sparse_mla(s, lat_np[lat_l], case.fmt, q_bits, d["rope_dim"], gi, gl,
                               d["softmax_scale"], d["ssmax_s"], rows=rows)
         go = O.decode_bf16(t_np(run.out[l][rows]))
+        gls = t_np(run.lse[l][rows])
         eo = check_close(go, o, f"{case.name} L{l} out")
-        el = check_close(t_np(run.lse[l][rows]), lse, f"{case.name} L{l} lse")
+        el = check_close(gls, lse, f"{case.name} L{l} lse")
         _say(f"  layer {l}: attention max|d| out {eo:.3e} lse {el:.3e}")
+        # end to end: attention on the oracle's own selection (the source layer's for a
+        # shared-indexer layer)
+        src = d["topk_source_layer"] if d["topk_source_layer"] >= 0 else l
+        oi_all, ol_all = gi.copy(), gl.copy()
+        same = True
+        for i, r in enumerate(rows):
+            oi, on = own_sets[src][i]
+            oi_all[r], ol_all[r] = oi, on
+            same &= bool(on == int(gl[r]) and np.array_equal(oi, gi[r]))
+        o2, lse2 = O.sparse_mla(s, lat_np[lat_l], case.fmt, q_bits, d["rope_dim"], oi_all,
+                                ol_all, d["softmax_scale"], d["ssmax_s"], rows=rows)
+        e2o = float(np.abs(go - o2).max())
+        e2l = float(np.abs(gls - lse2).max())
+        _say(f"  layer {l}: end to end on the oracle's own top-k (sets equal: {same}): "
+             f"max|d| out {e2o:.3e} lse {e2l:.3e}")
+        if same:
+            check_close(go, o2, f"{case.name} L{l} end-to-end out")
+            check_close(gls, lse2, f"{case.name} L{l} end-to-end lse")
 
 
 def test_full_size_second_layouts_sampled_rows():

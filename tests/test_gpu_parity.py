@@ -412,3 +412,55 @@ def test_device_faults_are_reported_and_contained():
     # a bit already set by the host is reported as is
     fault.fill_(-(1 << 31))              # bit 31, as an int32
     assert M.ml4_fault_query(fault) == 1 << 31
+
+
+def test_fp8_ds_mla_range_fault_is_reported_and_contained():
+    """The fp8_ds_mla MLA computes on fp16: a bf16 query element beyond 65,504 (row 1) and a
+    selected key whose latent scale exceeds 128 (one of row 2's keys) each raise
+    ML4_FAULT_RANGE; rows that touch neither are bit-identical to the clean run."""
+    case = CASES["c2_decode_ragged"]
+    _say("[gpu] fp8_ds_mla range fault: query element 7.0e4 in row 1, key scale 200 in row 2")
+    d = case.layers[0]
+    idx, ln = _topk_lists(case, 300, d["top_k"])
+    s = batch_np(case.batch)
+
+    def run_mla(c):
+        dev = synth.case_to(c, DEV)
+        run = CaseRunner(dev)
+        out = torch.empty_like(run.out[0])
+        lse = torch.empty_like(run.lse[0])
+        fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+        M.ml4_sparse_mla_decode(run.seqs, run.lat_caches[0], dev.inputs[0].q_mla, run.qm_dtype,
+                                case.mla_heads, d["rope_dim"], torch.from_numpy(idx).to(DEV),
+                                torch.from_numpy(ln).to(DEV), d["top_k"], d["softmax_scale"],
+                                d["ssmax_s"], out, run.qm_dtype, lse, run.ws, run.ws_bytes,
+                                fault)
+        torch.cuda.synchronize()
+        return out.cpu(), lse.cpu(), M.ml4_fault_query(fault)
+
+    o0, l0, f0 = run_mla(case)
+    assert f0 == 0
+    bad = synth.case_to(case, "cpu")
+    q = bad.inputs[0].q_mla.clone()
+    q[1, 5, 100] = 70000.0                       # bf16 70144 > 65504
+    assert float(q[1, 5, 100]) > 65504.0
+    pool = bad.inputs[0].lat_pool.clone()
+    t = int(idx[2, ln[2] // 2])                  # a key row 2 selects
+    b2 = int(np.searchsorted(s.q_start, 2, side="right") - 1)
+    blk, off = int(s.block_table[b2, t // s.block_size]), t % s.block_size
+    pool[blk, off, 512 + 4:512 + 8] = torch.tensor([200.0], dtype=torch.float32).view(torch.uint8)
+    bad.inputs[0].q_mla, bad.inputs[0].lat_pool = q, pool
+    clean_rows = []
+    for r in range(s.total_q):
+        if r in (1, 2):
+            continue
+        b = int(np.searchsorted(s.q_start, r, side="right") - 1)
+        slots = {int(s.block_table[b, int(p) // s.block_size]) * s.block_size
+                 + int(p) % s.block_size for p in idx[r, :ln[r]]}
+        assert blk * s.block_size + off not in slots
+        clean_rows.append(r)
+    o1, l1, f1 = run_mla(bad)
+    assert f1 == M.ML4_FAULT_RANGE
+    assert clean_rows
+    for r in clean_rows:
+        assert torch.equal(o1[r], o0[r]) and torch.equal(l1[r], l0[r]), f"row {r} changed"
