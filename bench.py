@@ -100,9 +100,9 @@ def algorithmic_work(case):
     return out
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current
-    kernel source (else None)."""
+    kernel source and on this workload (else None)."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(p):
         return None
@@ -110,7 +110,7 @@ def load_traffic(kernel: str):
         t = json.load(open(p))
     except Exception:
         return None
-    if t.get("source_sha256_16") != kernel_hash(kernel):
+    if t.get("source_sha256_16") != kernel_hash(kernel) or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -638,7 +638,7 @@ def main():
                               "topk": "k_topk_cand"}[dom]
         roof["layer"] = l0
         roof["avg_launch_us"] = us
-        roof["traffic"] = load_traffic(dom)
+        roof["traffic"] = load_traffic(dom, case.name)
         result["roofline"] = roof
     if not args.no_graph:
         result["graph_step"] = time_graph_step(run, K)
