@@ -81,11 +81,10 @@ enum ml4_fault_bits {
   ML4_FAULT_TOPK_INDEX = 1u << 1,  /* topk entry outside [0, q_pos] or topk_len > top_k    */
   ML4_FAULT_NAN_SCORE = 1u << 2,   /* a candidate score was NaN (ranked below -inf)        */
   ML4_FAULT_QPOS = 1u << 3,        /* q_pos outside [0, seq_len) or > max_seq_len - 1      */
-  ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a bf16 latent-query element beyond the fp16
-                                      range (|x| > 65504) or NaN, or a selected key's latent
-                                      scale with |s| > 128 or NaN; plain-E4M3 MLA: a
-                                      non-finite query scale; that row's output is
-                                      unspecified                                          */
+  ML4_FAULT_RANGE = 1u << 4        /* fp8 MLA: a non-finite bf16 latent-query element, or a
+                                      selected key's latent scale with |s| > 128 or NaN;
+                                      plain-E4M3 MLA: a non-finite query scale; that row's
+                                      output is unspecified                                */
 };
 
 /* A batch of requests.  [host] struct; the arrays are device memory.
@@ -171,10 +170,10 @@ int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, i
  *   out      [total_q][n_heads][512]: bf16 (ML4_BF16) for the fp8 and bf16 caches, fp32 for
  *            the fp32 cache.   lse: fp32 [total_q][n_heads] or NULL.
  *   ws       ml4_workspace_bytes(ML4_ENTRY_MLA, ...) bytes (split-K partials; may be 0).
- * Dequantisation of e4m3 codes is exact.  With the fp8 cache the latent QK and PV products
- * run on fp16 MFMA and the RoPE product on bf16 MFMA, all with fp32 accumulation: the bf16
- * latent query is rounded to fp16 (an element beyond the fp16 range raises
- * ML4_FAULT_RANGE), the softmax weights are rounded to fp16 after the running-max shift.
+ * Dequantisation of e4m3 codes is exact.  With the fp8 cache the QK products (latent and
+ * RoPE) run on bf16 MFMA with the query as given (e4m3 codes are bf16 values; a non-finite
+ * query element raises ML4_FAULT_RANGE) and PV on fp16 MFMA, all with fp32 accumulation;
+ * the softmax weights are rounded to fp16 after the running-max shift.
  * With the bf16 cache QK and the RoPE product run on bf16 MFMA with the query as given and
  * PV on fp16 MFMA (the latent values must lie within the fp16 range).
  */

@@ -13,12 +13,12 @@
 //   gather  the selected 656-byte rows (slot = block_table[t / bs] * bs + t % bs) straight
 //           into a three-tile LDS ring with 16-byte global->LDS transfers, issued two tiles
 //           ahead of the math; the rows keep the cache layout and are never rewritten;
-//   QK      S^T = K . Q^T with keys on M and heads on N.  Latent K fragments are read as
-//           e4m3 and decoded exactly to fp16 in registers for v_mfma_f32_16x16x32_f16 (the
-//           bf16 query is rounded to fp16, a value beyond its range is reported); each wave
-//           contracts one half of the latent dims (its two 128-dim scale blocks, each summed
-//           on its own and multiplied by its key's scale in fp32) and half of the RoPE dims on
-//           v_mfma_f32_16x16x32_bf16 with both operands exact, for 32 heads; the partner
+//   QK      S^T = K . Q^T with keys on M and heads on N, on v_mfma_f32_16x16x32_bf16 with
+//           the bf16 query as given: latent K fragments are read as e4m3 and decoded exactly
+//           to bf16 in registers (every e4m3 value is a bf16 value, and a product of two bf16
+//           values is exact in the fp32 accumulator); each wave contracts one half of the
+//           latent dims (its two 128-dim scale blocks, each summed on its own and multiplied
+//           by its key's scale in fp32) and half of the RoPE dims, for 32 heads; the partner
 //           wave's half arrives through LDS (a NoPE layer never touches the RoPE bytes);
 //   softmax online, base 2, per head = per lane column; the running maximum only moves when
 //           a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled;
@@ -53,7 +53,6 @@ constexpr uint32_t kFaultRange = 1u << 4;
 
 // Source of the gather for masked keys and for lanes past the end of a tile.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
-constexpr float kF16Max = 65504.0f;
 constexpr int kMaxSplitKeys = 2048;   // top_k <= 2048
 constexpr int kMlaThreads = 512;
 constexpr int kMlaWaves = 8;
@@ -149,11 +148,10 @@ constexpr int kQkAhead = 2;   // bf16 K fragments in flight ahead of the MFMAs
 // Scale offset of an fp8_ds_mla row.
 constexpr int kScaleOff = 512;
 
-// Query fragments per head tile: fp16 for the fp8_ds_mla rows (decoded exactly to fp16),
-// bf16 as given for the bf16 rows (8 x 32 dims each), E4M3 codes for the plain E4M3 rows
-// (two 128-dim latent fragments and one RoPE fragment, 32 bytes per lane each).
-template <int FMT> struct QFrag { typedef f16x8 type; static constexpr int N = 8; };
-template <> struct QFrag<kFmtBf16> { typedef bf16x8 type; static constexpr int N = 8; };
+// Query fragments per head tile: bf16 as given for the fp8_ds_mla and the bf16 rows (8 x 32
+// dims each), E4M3 codes for the plain E4M3 rows (two 128-dim latent fragments and one
+// RoPE fragment, 32 bytes per lane each).
+template <int FMT> struct QFrag { typedef bf16x8 type; static constexpr int N = 8; };
 template <> struct QFrag<kFmtE4m3> { typedef i32x8 type; static constexpr int N = 3; };
 
 // Eight bf16 values (four per 64-bit half) -> fp16, exactly for |x| in [2^-14, 65504]
@@ -178,8 +176,8 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const s16x4& lo, const s16x4& hi)
 
 // Partial S^T of key sub-tile kt over this wave's dims: rows = keys 16 kt + 4 g + j, columns
 // = heads.  K fragments are read as e4m3 (8 bytes per lane, all eight issued first) and
-// decoded exactly to fp16 in registers; the two latent blocks are accumulated apart and
-// scaled by their key's scale; the RoPE part runs on bf16 MFMA with both operands exact.
+// decoded exactly to bf16 in registers; the two latent blocks are accumulated apart and
+// scaled by their key's scale; the RoPE part runs on the same bf16 MFMA.
 template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* qr_lane,
                                         const typename QFrag<FMT>::type (&qb)[2][QFrag<FMT>::N],
@@ -269,15 +267,15 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_barrier(0);
     const u32x4 w = kw[i >> 1];
-    const f16x4 lo = e4m3x4_to_f16((i & 1) ? w[2] : w[0]);
-    const f16x4 hi = e4m3x4_to_f16((i & 1) ? w[3] : w[1]);
-    const f16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bf16x4 lo = e4m3x4_to_bf16((i & 1) ? w[2] : w[0]);
+    const bf16x4 hi = e4m3x4_to_bf16((i & 1) ? w[3] : w[1]);
+    const bf16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     if (i < 4) {
-      t0[0] = mfma_f16(k, qb[0][i], t0[0]);
-      t0[1] = mfma_f16(k, qb[1][i], t0[1]);
+      t0[0] = mfma_bf16(k, qb[0][i], t0[0]);
+      t0[1] = mfma_bf16(k, qb[1][i], t0[1]);
     } else {
-      t1[0] = mfma_f16(k, qb[0][i], t1[0]);
-      t1[1] = mfma_f16(k, qb[1][i], t1[1]);
+      t1[0] = mfma_bf16(k, qb[0][i], t1[0]);
+      t1[1] = mfma_bf16(k, qb[1][i], t1[1]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -533,15 +531,10 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       // 16 g + 8 (i%2) ..), bf16 rows take dims 32 i + 8 g ..
       const int qo = FMT == kFmtFp8 ? 64 * (i >> 1) + 16 * g16 + 8 * (i & 1) : 32 * i + 8 * g16;
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + qo);
-      if constexpr (FMT == kFmtBf16) {
-        qb[ht][i] = v;                   // bf16 rows: bf16 MFMA, the query as given
-      } else {
+      qb[ht][i] = v;                     // bf16 MFMA, the query as given
+      if constexpr (FMT == kFmtFp8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = (float)v[e];
-          q_range &= fabsf(f) <= kF16Max;
-          qb[ht][i][e] = (_Float16)f;    // exact for bf16 values inside the fp16 range
-        }
+        for (int e = 0; e < 8; ++e) q_range &= fabsf((float)v[e]) <= 3.4028235e38f;   // finite
       }
     }
     }

@@ -415,11 +415,11 @@ def test_device_faults_are_reported_and_contained():
 
 
 def test_fp8_ds_mla_range_fault_is_reported_and_contained():
-    """The fp8_ds_mla MLA computes on fp16: a bf16 query element beyond 65,504 (row 1) and a
-    selected key whose latent scale exceeds 128 (one of row 2's keys) each raise
-    ML4_FAULT_RANGE; rows that touch neither are bit-identical to the clean run."""
+    """A non-finite bf16 query element (row 1) and a selected key whose latent scale exceeds
+    128 (one of row 2's keys; P * scale must stay in fp16) each raise ML4_FAULT_RANGE; rows
+    that touch neither are bit-identical to the clean run."""
     case = CASES["c2_decode_ragged"]
-    _say("[gpu] fp8_ds_mla range fault: query element 7.0e4 in row 1, key scale 200 in row 2")
+    _say("[gpu] fp8_ds_mla range fault: query element inf in row 1, key scale 200 in row 2")
     d = case.layers[0]
     idx, ln = _topk_lists(case, 300, d["top_k"])
     s = batch_np(case.batch)
@@ -442,8 +442,7 @@ def test_fp8_ds_mla_range_fault_is_reported_and_contained():
     assert f0 == 0
     bad = synth.case_to(case, "cpu")
     q = bad.inputs[0].q_mla.clone()
-    q[1, 5, 100] = 70000.0                       # bf16 70144 > 65504
-    assert float(q[1, 5, 100]) > 65504.0
+    q[1, 5, 100] = float("inf")
     pool = bad.inputs[0].lat_pool.clone()
     t = int(idx[2, ln[2] // 2])                  # a key row 2 selects
     b2 = int(np.searchsorted(s.q_start, 2, side="right") - 1)
@@ -464,3 +463,33 @@ def test_fp8_ds_mla_range_fault_is_reported_and_contained():
     assert clean_rows
     for r in clean_rows:
         assert torch.equal(o1[r], o0[r]) and torch.equal(l1[r], l0[r]), f"row {r} changed"
+
+
+def test_fp8_ds_mla_query_beyond_fp16_range_matches_oracle():
+    """The bf16 query is taken as given: a head whose query elements exceed the fp16 range
+    (row 0, head 3, times 2^15: up to ~1e5) matches the oracle and raises nothing."""
+    case = CASES["c2_decode_ragged"]
+    d = case.layers[0]
+    _say("[gpu] fp8_ds_mla query beyond fp16 range")
+    big = synth.case_to(case, "cpu")
+    q = big.inputs[0].q_mla.clone()
+    q[0, 3] = q[0, 3] * 32768.0                  # exact in bf16 (a power of two)
+    assert float(q[0, 3].float().abs().max()) > 65504.0
+    big.inputs[0].q_mla = q
+    idx, ln = _topk_lists(case, 301, d["top_k"])
+    dev = synth.case_to(big, DEV)
+    run = CaseRunner(dev)
+    s = batch_np(case.batch)
+    out = torch.empty_like(run.out[0])
+    lse = torch.empty_like(run.lse[0])
+    M.ml4_sparse_mla_decode(run.seqs, run.lat_caches[0], dev.inputs[0].q_mla, run.qm_dtype,
+                            case.mla_heads, d["rope_dim"], torch.from_numpy(idx).to(DEV),
+                            torch.from_numpy(ln).to(DEV), d["top_k"], d["softmax_scale"],
+                            d["ssmax_s"], out, run.qm_dtype, lse, run.ws, run.ws_bytes, run.fault)
+    torch.cuda.synchronize()
+    assert run.fault_bits() == 0
+    o, l_ref = O.sparse_mla(s, t_np(big.inputs[0].lat_pool), "fp8", t_np(q), d["rope_dim"], idx,
+                            ln, d["softmax_scale"], d["ssmax_s"])
+    eo = check_close(_decode_out(case, out), o, "out")
+    el = check_close(t_np(lse), l_ref, "lse")
+    _say(f"  max|d| out {eo:.3e} lse {el:.3e}")
