@@ -21,7 +21,10 @@
 //           by its key's scale in fp32) and half of the RoPE dims, for 32 heads; the partner
 //           wave's half arrives through LDS (a NoPE layer never touches the RoPE bytes);
 //   softmax online, base 2, per head = per lane column; the running maximum only moves when
-//           a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled;
+//           a tile exceeds it by more than 2^8, so the accumulator is rarely rescaled; the
+//           logit scale rides in the exponent's fma, and keys without a slot are masked only
+//           in tiles whose validity mask (one ballot per tile, built with the slot table)
+//           says they hold one;
 //   PV      O^T = V^T . P^T on v_mfma_f32_16x16x32_f16 with latent columns on M, heads on
 //           N, over the wave's 256 latent dims: V^T fragments come from the e4m3 rows through
 //           ds_read_b64_tr_b8 and are decoded in registers, P^T comes from the QK
@@ -128,7 +131,8 @@ struct MlaGeom {
   static constexpr int XS_WORDS = kMlaWaves * 4 * kWave;            // f32x4 per buffer
   static constexpr int OFF_QR = OFF_XS + XS_BUFS * XS_WORDS * 16;    // [128][kQRS] bf16
   static constexpr int OFF_SLOT = OFF_QR + (ROPE && FMT != kFmtE4m3 ? kHeadsPerWg * kQRS * 2 : 0);
-  static constexpr int BYTES = OFF_SLOT + kMaxSplitKeys * 4;
+  static constexpr int OFF_MASK = OFF_SLOT + kMaxSplitKeys * 4;        // [tiles] u32
+  static constexpr int BYTES = OFF_MASK + (kMaxSplitKeys / kTK) * 4;
 };
 static_assert(MlaGeom<64, kFmtFp8>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<64, kFmtBf16>::BYTES <= 160 * 1024, "LDS budget");
@@ -174,10 +178,8 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const s16x4& lo, const s16x4& hi)
   return r;
 }
 
-// Partial S^T of key sub-tile kt over this wave's dims: rows = keys 16 kt + 4 g + j, columns
-// = heads.  K fragments are read as e4m3 (8 bytes per lane, all eight issued first) and
-// decoded exactly to bf16 in registers; the two latent blocks are accumulated apart and
-// scaled by their key's scale; the RoPE part runs on the same bf16 MFMA.
+// Partial S^T of key sub-tile kt over this wave's dims for the bf16 and plain E4M3 rows:
+// rows = keys 16 kt + 4 g + j (+ the interleave of the row layout), columns = heads.
 template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* qr_lane,
                                         const typename QFrag<FMT>::type (&qb)[2][QFrag<FMT>::N],
@@ -255,57 +257,91 @@ __device__ __forceinline__ void qk_part(const unsigned char* raw, const __bf16* 
     for (int ht = 0; ht < 2; ++ht) sk[ht] = (t0[ht] + t1[ht]) + tr[ht];
     return;
   }
-  if constexpr (FMT == kFmtFp8) {
-  // Key c of sub-tile kt sits in LDS row 2c + kt; lane (g, c) reads 16 bytes per pair of
-  // k-steps (dims 64 jj + 16 g .. +15 of the half).  Both choices make every half-wave's
-  // 16-byte reads hit distinct bank groups.
-  const unsigned char* krow = raw + (2 * c16 + kt) * RS + 256 * DH + 16 * g16;
-  u32x4 kw[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) kw[jj] = *reinterpret_cast<const u32x4*>(krow + 64 * jj);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    const u32x4 w = kw[i >> 1];
-    const bf16x4 lo = e4m3x4_to_bf16((i & 1) ? w[2] : w[0]);
-    const bf16x4 hi = e4m3x4_to_bf16((i & 1) ? w[3] : w[1]);
-    const bf16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    if (i < 4) {
-      t0[0] = mfma_bf16(k, qb[0][i], t0[0]);
-      t0[1] = mfma_bf16(k, qb[1][i], t0[1]);
-    } else {
-      t1[0] = mfma_bf16(k, qb[0][i], t1[0]);
-      t1[1] = mfma_bf16(k, qb[1][i], t1[1]);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if (ROPE) {
-    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(
-        raw + (2 * c16 + kt) * RS + G::ROPE_OFF + 2 * (32 * DH + 8 * g16));
-    const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
-    const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
-    tr[0] = mfma_bf16(kr, q0, tr[0]);
-    tr[1] = mfma_bf16(kr, q1, tr[1]);
-  }
-  f32x2 sc[4];   // scales of keys 4 g + j of the sub-tile (LDS rows 2 (4 g + j) + kt)
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    sc[j] = *reinterpret_cast<const f32x2*>(raw + (2 * (4 * g16 + j) + kt) * RS + kScaleOff +
-                                            8 * DH);
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      sk[ht][j] = fmaf(t1[ht][j], sc[j][1], fmaf(t0[ht][j], sc[j][0], tr[ht][j]));
-  }
+  static_assert(FMT == kFmtBf16, "fp8_ds_mla tiles take qk_tile_fp8");
   }
 }
 
-// O^T[256 DH .. +255][32 heads] += V^T P^T, V's per-128 scale folded into P.  V^T fragments
-// come straight from the e4m3 rows through ds_read_b64_tr_b8: in lane group g, lane pair
-// (2e, 2e+1) addresses the LDS row of key 4 g + (e & 3) of sub-tile e >> 2 (bytes 8 (lane & 1)
-// of the fragment's 16 dims), and lane (g, i) receives dim i of those eight rows -- the key
-// order of the P^T operand taken from the S^T accumulators in place.
+// Both key sub-tiles of an fp8_ds_mla tile, partial S^T written to this wave's exchange
+// slot.  LDS reads are issued while earlier matrix work runs, into registers that consumed
+// K words free: the RoPE fragments after the fourth latent k-step; the scales after the
+// fourth (NoPE) or after the last (RoPE: no registers earlier); the next sub-tile's K words
+// as soon as this one's are consumed (NoPE only, for the same reason).  Each placement
+// measured faster than reading at use (C3: RoPE -2.5 %, NoPE -4.7 %), with no spills.
+template <int ROPE, int DH>
+__device__ __forceinline__ void qk_tile_fp8(const unsigned char* raw, const __bf16* qr_lane,
+                                            const bf16x8 (&qb)[2][8], f32x4* mine, int lane,
+                                            int g16, int c16) {
+  constexpr int RS = MlaGeom<ROPE, kFmtFp8>::RS;
+  constexpr int ROPE_OFF = MlaGeom<ROPE, kFmtFp8>::ROPE_OFF;
+  constexpr int kRopeAt = 4, kScaleAt = ROPE ? 8 : 4;   // k-step before which they are read
+  constexpr bool kNextEarly = ROPE == 0;
+  u32x4 kw[4];
+  auto load_k = [&](int kt) {
+    const unsigned char* krow = raw + (2 * c16 + kt) * RS + 256 * DH + 16 * g16;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) kw[jj] = *reinterpret_cast<const u32x4*>(krow + 64 * jj);
+  };
+  load_k(0);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x4 t0[2], t1[2], tr[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      t0[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      t1[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tr[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bf16x8 kr, q0, q1;
+    f32x2 sc[4];   // scales of keys 4 g + j of the sub-tile (LDS rows 2 (4 g + j) + kt)
+    auto load_rope = [&]() {
+      kr = *reinterpret_cast<const bf16x8*>(raw + (2 * c16 + kt) * RS + ROPE_OFF +
+                                            2 * (32 * DH + 8 * g16));
+      q0 = *reinterpret_cast<const bf16x8*>(qr_lane);
+      q1 = *reinterpret_cast<const bf16x8*>(qr_lane + 16 * kQRS);
+    };
+    auto load_sc = [&]() {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc[j] = *reinterpret_cast<const f32x2*>(raw + (2 * (4 * g16 + j) + kt) * RS +
+                                                kScaleOff + 8 * DH);
+    };
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ROPE && i == kRopeAt) load_rope();
+      if (i == kScaleAt) load_sc();
+      const u32x4 w = kw[i >> 1];
+      const bf16x4 lo = e4m3x4_to_bf16((i & 1) ? w[2] : w[0]);
+      const bf16x4 hi = e4m3x4_to_bf16((i & 1) ? w[3] : w[1]);
+      const bf16x8 k{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (i < 4) {
+        t0[0] = mfma_bf16(k, qb[0][i], t0[0]);
+        t0[1] = mfma_bf16(k, qb[1][i], t0[1]);
+      } else {
+        t1[0] = mfma_bf16(k, qb[0][i], t1[0]);
+        t1[1] = mfma_bf16(k, qb[1][i], t1[1]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kNextEarly && kt == 0) load_k(1);
+    if (kScaleAt >= 8) load_sc();
+    if (ROPE) {
+      tr[0] = mfma_bf16(kr, q0, tr[0]);
+      tr[1] = mfma_bf16(kr, q1, tr[1]);
+    }
+    f32x4 sk[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sk[ht][j] = fmaf(t1[ht][j], sc[j][1], fmaf(t0[ht][j], sc[j][0], tr[ht][j]));
+    mine[(2 * kt) * kWave + lane] = sk[0];
+    mine[(2 * kt + 1) * kWave + lane] = sk[1];
+    if (!kNextEarly && kt == 0) load_k(1);
+  }
+}
+
+// O^T[256 DH .. +255][32 heads] += V^T P^T for the bf16 rows.
 template <int ROPE, int FMT, int DH>
 __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&pv)[2][2][4],
                                         f32x4 (&o_acc)[2][16], bool& sc_bad, int g16,
@@ -338,54 +374,74 @@ __device__ __forceinline__ void pv_part(const unsigned char* raw, const float (&
     __builtin_amdgcn_sched_barrier(0);
     (void)sc_bad;
     return;
-  } else {
-  // LDS row of P^T's K-index e in lane group g: key 4 g + (e & 3) of sub-tile e >> 2.
+  }
+  static_assert(FMT == kFmtBf16, "e4m3-coded rows take pv_tile");
+}
+
+// PV of the e4m3-coded rows (fp8_ds_mla and plain E4M3) over the wave's two 128-dim blocks
+// as one stream of 16 fragment steps: the transposed V reads run four steps ahead across the
+// block boundary, and the second block's scales (fp8_ds_mla) are read while the first
+// block's matrix work runs.  Plain E4M3 rows have no per-key scales: P as is, the
+// per-tensor scale applied to the normalised output.  V^T fragments come straight from the
+// e4m3 rows through ds_read_b64_tr_b8: in lane group g, lane pair (2e, 2e+1) addresses the
+// LDS row of P^T's K-index e (bytes 8 (lane & 1) of the fragment's 16 dims), and lane (g, i)
+// receives dim i of those eight rows -- the key order of the P^T operand taken from the S^T
+// accumulators in place.  V's per-128 scale is folded into P per block.
+template <int ROPE, int FMT, int DH>
+__device__ __forceinline__ void pv_tile(const unsigned char* raw, const float (&pv)[2][2][4],
+                                        f32x4 (&o_acc)[2][16], bool& sc_bad, int g16, int c16) {
+  static_assert(FMT == kFmtFp8 || FMT == kFmtE4m3, "e4m3-coded rows");
+  constexpr int RS = MlaGeom<ROPE, FMT>::RS;
+  constexpr bool SC = FMT == kFmtFp8;
+  // LDS row of P^T's K-index e in lane group g: key 4 g + (e & 3) of sub-tile e >> 2
+  // (fp8_ds_mla tiles interleave the two sub-tiles' rows).
   auto kp_row = [&](int e) {
-    return FMT == kFmtFp8 ? 2 * (4 * g16 + (e & 3)) + (e >> 2) : 16 * (e >> 2) + 4 * g16 + (e & 3);
+    return SC ? 2 * (4 * g16 + (e & 3)) + (e >> 2) : 16 * (e >> 2) + 4 * g16 + (e & 3);
   };
-  const int e2 = c16 >> 1;
-  const int kp = kp_row(e2);
-  const unsigned char* vbase = raw + kp * RS + 256 * DH + 8 * (c16 & 1);
-#pragma unroll
-  for (int b2 = 0; b2 < 2; ++b2) {
-    const int blk = 2 * DH + b2;
-    float vsc[8];   // per-key scale of this 128-dim block (the per-tensor scale comes later)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vsc[e] = FMT == kFmtE4m3 ? 1.0f : *reinterpret_cast<const float*>(
-          raw + kp_row(e) * RS + kScaleOff + 4 * blk);
-    typedef int v2i __attribute__((ext_vector_type(2)));
-    auto read_v = [&](int dd) {
-      return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) v2i*)(const_cast<unsigned char*>(
-              vbase + 16 * (b2 * 8 + dd))));
-    };
-    v2i vw[8];
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) vw[dd] = read_v(dd);
-    f16x8 pb[2];
+  const unsigned char* vbase = raw + kp_row(c16 >> 1) * RS + 256 * DH + 8 * (c16 & 1);
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  auto read_v = [&](int d) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(const_cast<unsigned char*>(vbase + 16 * d)));
+  };
+  float vsc[8];
+  auto load_sc = [&](int b2) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (FMT == kFmtFp8) sc_bad |= !(fabsf(vsc[e]) <= kMaxVScale);
+      vsc[e] = *reinterpret_cast<const float*>(raw + kp_row(e) * RS + kScaleOff +
+                                               4 * (2 * DH + b2));
+  };
+  f16x8 pb[2];
+  auto make_pb = [&]() {
+    if constexpr (SC) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc_bad |= !(fabsf(vsc[e]) <= kMaxVScale);
+    }
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        pb[ht][e] = FMT == kFmtE4m3 ? (_Float16)pv[ht][e >> 2][e & 3]
-                                    : (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e]);
+        pb[ht][e] = SC ? (_Float16)(pv[ht][e >> 2][e & 3] * vsc[e])
+                       : (_Float16)pv[ht][e >> 2][e & 3];
+  };
+  v2i vw[4];
+  if (SC) load_sc(0);
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (dd + 4 < 8) vw[dd + 4] = read_v(dd + 4);
-      const v2i w = vw[dd];
-      const f16x4 lo = e4m3x4_to_f16((uint32_t)w[0]), hi = e4m3x4_to_f16((uint32_t)w[1]);
-      const f16x8 va{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o_acc[0][b2 * 8 + dd] = mfma_f16(va, pb[0], o_acc[0][b2 * 8 + dd]);
-      o_acc[1][b2 * 8 + dd] = mfma_f16(va, pb[1], o_acc[1][b2 * 8 + dd]);
-    }
+  for (int d = 0; d < 4; ++d) vw[d] = read_v(d);
+  make_pb();
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
     __builtin_amdgcn_sched_barrier(0);
+    if (SC && d == 8) make_pb();
+    const v2i w = vw[d & 3];
+    if (d + 4 < 16) vw[d & 3] = read_v(d + 4);
+    if (SC && d == 4) load_sc(1);
+    const f16x4 lo = e4m3x4_to_f16((uint32_t)w[0]), hi = e4m3x4_to_f16((uint32_t)w[1]);
+    const f16x8 va{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    o_acc[0][d] = mfma_f16(va, pb[0], o_acc[0][d]);
+    o_acc[1][d] = mfma_f16(va, pb[1], o_acc[1][d]);
   }
-  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int ROPE, int FMT>
@@ -397,6 +453,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   f32x4* xs = reinterpret_cast<f32x4*>(smem + G::OFF_XS);
   __bf16* qr_sh = reinterpret_cast<__bf16*>(smem + G::OFF_QR);
   int* slot_sh = reinterpret_cast<int*>(smem + G::OFF_SLOT);
+  uint32_t* mask_sh = reinterpret_cast<uint32_t*>(smem + G::OFF_MASK);
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
 
@@ -450,6 +507,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       }
     }
     slot_sh[i] = slot;
+    // Bit k of a tile's mask: its k-th selected key has a slot.  A wave's 64 entries are
+    // two whole tiles (i - lane is a multiple of 64), so one ballot gives both masks.
+    const uint64_t ok = __ballot(slot >= 0);
+    if (lane0 == 0) {
+      mask_sh[i >> 5] = (uint32_t)ok;
+      if ((i >> 5) + 1 < ntiles) mask_sh[(i >> 5) + 1] = (uint32_t)(ok >> 32);
+    }
   }
   // RoPE query of the group's heads (bf16, as given) into LDS.
   if (ROPE && FMT != kFmtE4m3) {
@@ -543,6 +607,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const float qk_scale = a.softmax_scale * ssmax_mult(a.ssmax_s, row_ok ? p : 0) * kLog2e;
   qks[0] *= qk_scale;
   qks[1] *= qk_scale;
+  if constexpr (FMT != kFmtE4m3) {
+    // The scale is zero only under SSMax at position 0, where the row has one key and every
+    // positive scale gives the same softmax; the smallest normal float keeps masked keys'
+    // -inf logits at -inf (0 * -inf would be NaN).
+    qks[0] = fmaxf(qks[0], 1.17549435e-38f);
+    qks[1] = fmaxf(qks[1], 1.17549435e-38f);
+  }
 
   f32x4 o_acc[2][16];
 #pragma unroll
@@ -586,6 +657,10 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     if (active) {
       const __bf16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
       f32x4* mine = xsb + wave * 4 * kWave;
+      if constexpr (FMT == kFmtFp8) {
+        if (dh == 0) qk_tile_fp8<ROPE, 0>(raw, qr_lane, qb, mine, lane, g16, c16);
+        else qk_tile_fp8<ROPE, 1>(raw, qr_lane, qb, mine, lane, g16, c16);
+      } else {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 sk[2];
@@ -594,7 +669,24 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         mine[(2 * kt) * kWave + lane] = sk[0];
         mine[(2 * kt + 1) * kWave + lane] = sk[1];
       }
+      }
     }
+    // Both halves' partial S of this wave's heads and the tile's key mask, read after the
+    // barrier.  (Reading them before the gather of tile + 2 is issued spills.)
+    f32x4 ps0[2][2], ps1[2][2];
+    uint32_t vmask = 0;
+    auto load_partials = [&]() {
+      const f32x4* p0 = xsb + (2 * hg) * 4 * kWave;
+      const f32x4* p1 = xsb + (2 * hg + 1) * 4 * kWave;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          ps0[kt][ht] = p0[(2 * kt + ht) * kWave + lane];
+          ps1[kt][ht] = p1[(2 * kt + ht) * kWave + lane];
+        }
+      vmask = mask_sh[tile];
+    };
     if constexpr (G::ONEBAR) {
       // Only tile + 1's transfers are outstanding.  After the barrier every wave's partial
       // S of this tile and tile + 1 are in LDS, and every wave is done with tile - 1, whose
@@ -602,32 +694,42 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       wait_vmcnt<0>();
       __syncthreads();
       if (tile + 2 < ntiles) issue(tile + 2, lane);
+      if (active) load_partials();
     } else {
       __syncthreads();
+      if (active) load_partials();
     }
     if (!active) continue;
+    // Logits: half 0 + half 1 in the same order in both partners.  With a positive logit
+    // scale c (every format but plain E4M3, whose per-head query scale may take any sign) c
+    // is applied inside the exponent's fma and the tile maximum is max(s) * c; otherwise the
+    // scaled logits are formed first.
+    constexpr bool FOLD = FMT != kFmtE4m3;
     float pv[2][2][4];
-    {
-      const f32x4* p0 = xsb + (2 * hg) * 4 * kWave;
-      const f32x4* p1 = xsb + (2 * hg + 1) * 4 * kWave;
-      // slots of accumulator keys (kt, 4 g + j): selection index 8 g + 2 j + kt with the
-      // interleaved rows of fp8_ds_mla tiles, 16 kt + 4 g + j otherwise
-      constexpr bool IL = FMT == kFmtFp8;
-      const int* sl = slot_sh + tile * kTK + (IL ? 8 : 4) * g16;
-      const int4 s0 = *reinterpret_cast<const int4*>(sl);
-      const int4 s1 = *reinterpret_cast<const int4*>(sl + (IL ? 4 : 16));
-      const int sv[2][4] = {{IL ? s0.x : s0.x, IL ? s0.z : s0.y, IL ? s1.x : s0.z, IL ? s1.z : s0.w},
-                            {IL ? s0.y : s1.x, IL ? s0.w : s1.y, IL ? s1.y : s1.z, IL ? s1.w : s1.w}};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const f32x4 sum = ps0[kt][ht] + ps1[kt][ht];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[ht][kt][j] = FOLD ? sum[j] : sum[j] * qks[ht];
+      }
+    // Keys without a slot (a tile's tail, masked keys) are rare: one uniform test skips the
+    // per-key masking for whole tiles.  Accumulator key (kt, 4 g + j) is selection index
+    // 8 g + 2 j + kt with the interleaved rows of fp8_ds_mla tiles, 16 kt + 4 g + j otherwise.
+    if (__builtin_amdgcn_readfirstlane(vmask) != 0xFFFFFFFFu) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-          const f32x4 sum = p0[(2 * kt + ht) * kWave + lane] + p1[(2 * kt + ht) * kWave + lane];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pv[ht][kt][j] = sv[kt][j] >= 0 ? sum[j] * qks[ht] : -__builtin_inff();
+        for (int j = 0; j < 4; ++j) {
+          const int bit = FMT == kFmtFp8 ? 8 * g16 + 2 * j + kt : 16 * kt + 4 * g16 + j;
+          if (!((vmask >> bit) & 1u)) pv[0][kt][j] = pv[1][kt][j] = -__builtin_inff();
         }
     }
+    auto weight = [&](int ht, int kt, int j, float msub) {
+      return FOLD ? __builtin_amdgcn_exp2f(fmaf(pv[ht][kt][j], qks[ht], -msub))
+                  : __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub);
+    };
 
     // ---- online softmax (base 2) per head (lane column), identical in both partner waves.
     //      The vector-only phase runs at wave priority 1 (measured 1.5 % faster per tile than
@@ -644,13 +746,15 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ev[kt][j] = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub0);
+        for (int j = 0; j < 4; ++j) ev[kt][j] = weight(ht, kt, j, msub0);
       float mt = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mt = fmaxf(mt, pv[ht][kt][j]);
       mt = max_over_lane_groups(mt);
+      // max(s) * c == max(s * c) for c > 0 (rounding is monotonic).
+      if (FOLD) mt *= qks[ht];
       const bool need = mt > m_run[ht] + kRescaleSlack || (m_run[ht] == -__builtin_inff() && mt > m_run[ht]);
       if (__any(need)) {
         const float m_new = need ? fmaxf(m_run[ht], mt) : m_run[ht];
@@ -664,7 +768,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ev[kt][j] = __builtin_amdgcn_exp2f(pv[ht][kt][j] - msub);
+          for (int j = 0; j < 4; ++j) ev[kt][j] = weight(ht, kt, j, msub);
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -678,8 +782,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T over this wave's dim half
-    if (dh == 0) pv_part<ROPE, FMT, 0>(raw, pv, o_acc, sc_bad, g16, c16);
-    else pv_part<ROPE, FMT, 1>(raw, pv, o_acc, sc_bad, g16, c16);
+    if constexpr (FMT == kFmtBf16) {
+      if (dh == 0) pv_part<ROPE, FMT, 0>(raw, pv, o_acc, sc_bad, g16, c16);
+      else pv_part<ROPE, FMT, 1>(raw, pv, o_acc, sc_bad, g16, c16);
+    } else {
+      if (dh == 0) pv_tile<ROPE, FMT, 0>(raw, pv, o_acc, sc_bad, g16, c16);
+      else pv_tile<ROPE, FMT, 1>(raw, pv, o_acc, sc_bad, g16, c16);
+    }
   }
 
   if (__any(sc_bad) && lane0 == 0) raise_fault(a.fault, kFaultRange);
