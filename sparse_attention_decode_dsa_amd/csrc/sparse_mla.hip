@@ -470,6 +470,17 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int split = blockIdx.z;
   const SeqView& s = a.s;
   const int H = a.n_heads;
+  // This split's top-k indices, up to kMaxSplitKeys / NT per thread (entry i = tid + NT u),
+  // are loaded first, clamped to the row's top_k entries, so that they are in flight with
+  // the request lookup below; the row's length masks them afterwards.
+  constexpr int SPT = kMaxSplitKeys / NT;
+  const int k_begin = split * keys_per_split;
+  const int32_t* sel = a.window > 0 ? nullptr : a.idx + (size_t)r * a.top_k;
+  int tv[SPT];
+  if (sel) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) tv[u] = sel[min(k_begin + tid + NT * u, a.top_k - 1)];
+  }
   const int b = request_of_wave(s.q_start, s.batch, r);
   const int p = s.q_pos[r];
   bool row_ok = true;
@@ -484,37 +495,51 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
     nsel = max(0, min(nsel, a.top_k));
   }
   if (!row_ok) nsel = 0;
-  const int k_begin = split * keys_per_split;
   const int k_end = min(nsel, k_begin + keys_per_split);
   const int nkeys = max(0, k_end - k_begin);
   const int ntiles = (nkeys + kTK - 1) / kTK;
 
   // Physical slot of every selected key of this split (-1: outside [0, p] or bad block).
-  const int32_t* sel = a.window > 0 ? nullptr : a.idx + (size_t)r * a.top_k;
+  // Every block-table entry is loaded in one round (block 0 for a position outside [0, p],
+  // masked afterwards) rather than one dependent round per entry.
   const int32_t* bt = s.block_table + (size_t)b * s.mbps;
-  for (int i = tid; i < ntiles * kTK; i += NT) {
-    int slot = -1;
-    if (i < nkeys) {
-      const int t = a.window > 0 ? p - nsel + 1 + k_begin + i : sel[k_begin + i];
-      if (t < 0 || t > p) {
-        raise_fault(a.fault, kFaultTopk);
-      } else {
-        const int blk = bt[t >> s.lbs];
-        if ((unsigned)blk >= (unsigned long long)a.num_blocks)
-          raise_fault(a.fault, kFaultBlock);
-        else
-          slot = (blk << s.lbs) | (t & ((1 << s.lbs) - 1));
+  const int nent = ntiles * kTK;
+  bool bad_t = false, bad_b = false;
+  if (nkeys > 0) {
+    const unsigned long long num_blocks = (unsigned long long)a.num_blocks;
+    const int wbase = p - nsel + 1 + k_begin;
+    int bv[SPT];
+    if (!sel) {
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) tv[u] = wbase + tid + NT * u;
+    }
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const bool t_ok = tv[u] >= 0 && tv[u] <= p;
+      bv[u] = bt[t_ok ? tv[u] >> s.lbs : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int i = tid + NT * u;
+      const int t = tv[u];
+      int slot = -1;
+      if (i < nkeys) {
+        if (t < 0 || t > p) bad_t = true;
+        else if ((unsigned long long)(unsigned)bv[u] >= num_blocks) bad_b = true;
+        else slot = (bv[u] << s.lbs) | (t & ((1 << s.lbs) - 1));
+      }
+      if (i < nent) slot_sh[i] = slot;
+      // Bit k of a tile's mask: its k-th selected key has a slot.  A wave's 64 entries are
+      // two whole tiles (i - lane is a multiple of 64), so one ballot gives both masks.
+      const uint64_t ok = __ballot(slot >= 0);
+      if (lane0 == 0 && i < nent) {
+        mask_sh[i >> 5] = (uint32_t)ok;
+        if ((i >> 5) + 1 < ntiles) mask_sh[(i >> 5) + 1] = (uint32_t)(ok >> 32);
       }
     }
-    slot_sh[i] = slot;
-    // Bit k of a tile's mask: its k-th selected key has a slot.  A wave's 64 entries are
-    // two whole tiles (i - lane is a multiple of 64), so one ballot gives both masks.
-    const uint64_t ok = __ballot(slot >= 0);
-    if (lane0 == 0) {
-      mask_sh[i >> 5] = (uint32_t)ok;
-      if ((i >> 5) + 1 < ntiles) mask_sh[(i >> 5) + 1] = (uint32_t)(ok >> 32);
-    }
   }
+  if (bad_t) raise_fault(a.fault, kFaultTopk);
+  if (bad_b) raise_fault(a.fault, kFaultBlock);
   // RoPE query of the group's heads (bf16, as given) into LDS.
   if (ROPE && FMT != kFmtE4m3) {
     for (int i = tid; i < kHeadsPerWg * 8; i += NT) {
