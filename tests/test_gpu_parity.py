@@ -70,6 +70,11 @@ def small_cases():
         "h16_h64_blocks16": synth.make_case(
             "hx", 61, seq_lens=[900, 1500], q_per_seq=[2, 1], block_size=16, fmt="fp8",
             idx_heads=32, mla_heads=16, layers=[L(0, top_k=512, idx_ssmax_s=0.25)]),
+        # 11 and 8 rows per request: full 4-row indexer groups and a group of 3, with 32
+        # indexer heads and 16-token blocks
+        "r8_rows_h32": synth.make_case(
+            "r8", 91, seq_lens=[5000, 2300], q_per_seq=[11, 8], block_size=16, fmt="fp8",
+            idx_heads=32, mla_heads=64, layers=[L(0, top_k=1024, idx_ssmax_s=0.2)]),
     }
 
 
@@ -118,7 +123,8 @@ def test_layer_step_matches_oracle(name):
 
 @pytest.mark.parametrize("name", ["c1_fp32_4096", "c2_decode_ragged", "c3_verify_rope_nope",
                                   "c5_prefill_causal", "r2_verify_ragged", "h48_decode_rows",
-                                  "h16_decode_rows", "h32_decode_rows", "h16_h64_blocks16"])
+                                  "h16_decode_rows", "h32_decode_rows", "h16_h64_blocks16",
+                                  "r8_rows_h32"])
 def test_indexer_scores_match_oracle(name):
     case = CASES[name]
     _say(f"[gpu] indexer {name}")
