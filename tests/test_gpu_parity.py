@@ -70,11 +70,13 @@ def small_cases():
         "h16_h64_blocks16": synth.make_case(
             "hx", 61, seq_lens=[900, 1500], q_per_seq=[2, 1], block_size=16, fmt="fp8",
             idx_heads=32, mla_heads=16, layers=[L(0, top_k=512, idx_ssmax_s=0.25)]),
-        # 11 and 8 rows per request: full 4-row indexer groups and a group of 3, with 32
-        # indexer heads and 16-token blocks
+        # 11, 8 and 2 rows per request: full 4-row indexer groups and groups of 3 and 2, 32
+        # indexer heads, 16-token blocks; the last request's rows sit at positions 0 and 1,
+        # so with SSMax the attention logit scale of position 0 is zero (one key)
         "r8_rows_h32": synth.make_case(
-            "r8", 91, seq_lens=[5000, 2300], q_per_seq=[11, 8], block_size=16, fmt="fp8",
-            idx_heads=32, mla_heads=64, layers=[L(0, top_k=1024, idx_ssmax_s=0.2)]),
+            "r8", 91, seq_lens=[5000, 2300, 2], q_per_seq=[11, 8, 2], block_size=16,
+            fmt="fp8", idx_heads=32, mla_heads=64,
+            layers=[L(0, top_k=1024, idx_ssmax_s=0.2, ssmax_s=0.3)]),
     }
 
 
@@ -150,7 +152,8 @@ def test_indexer_scores_match_oracle(name):
         err = np.abs(g - f) / max(scale, 1e-30)
         assert err.max() <= SCORE_RTOL, f"row {r}: rel err {err.max():.3e}"
     rel = np.max([np.max(np.abs(got[r, :int(s.q_pos[r]) + 1] - ref[r, :int(s.q_pos[r]) + 1]) /
-                         np.abs(ref[r, :int(s.q_pos[r]) + 1]).max()) for r in range(s.total_q)])
+                         max(np.abs(ref[r, :int(s.q_pos[r]) + 1]).max(), 1e-30))
+                  for r in range(s.total_q)])
     _say(f"  max error relative to row max: {rel:.3e}")
 
 
