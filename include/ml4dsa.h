@@ -312,7 +312,8 @@ int ml4_sparse_attn_layer_static(const ml4_layer* layers, int32_t layer, const m
  *                the write entries treat as writable).  ML4_LAT_E4M3_576 goes through
  *                ml4_latent_cache_write_e4m3.
  *   block_size   tokens per block (power of two, 16 .. 65536).
- *   k / c        [n_tokens][128] / [n_tokens][512], BF16 or F32 (src_dtype).
+ *   k / c        [n_tokens][128] / [n_tokens][512], BF16 or F32 (src_dtype), 16-byte aligned
+ *                (rows are read as 16-byte vectors).
  *   k_rope       [n_tokens][64] bf16 with rope_dim 64; NULL with rope_dim 0 (NoPE: the RoPE
  *                bytes of the row are left untouched).
  *   slot_mapping [n_tokens] int64: destination slot = block_id * block_size + offset;

@@ -578,7 +578,7 @@ int cache_write(const char* entry, bool latent, bool e4m3, const ml4_cache* cach
   if (n_tokens > 0) {
     c.bad(!src, "source values are NULL");
     c.bad(!slot_mapping, "slot_mapping is NULL");
-    c.bad(!aligned(src, src_dtype == ML4_F32 ? 4 : 2), "source values misaligned");
+    c.bad(!aligned(src, 16), "source values must be 16-byte aligned");
     c.bad(!aligned(slot_mapping, 8), "slot_mapping must be 8-byte aligned");
   }
   if (latent) {

@@ -9,11 +9,13 @@
 // group scale = amax / 448 and code = E4M3(x / scale), round to nearest even, clamped to
 // +-448 (binary32 arithmetic); an all-zero group stores scale 0 and zero codes.
 //
-// One wave per token.  Index row: each lane converts two of the 128 values; the scale is a
-// wave-wide maximum.  Latent row: each lane converts eight of the 512 values, the 16 lanes of
-// a 128-value group reduce their maximum with xor shuffles, and lanes 0..15 copy the RoPE
-// bytes.  Both are streams: 256 B (bf16 key) or 1,160 B (bf16 latent + RoPE) read and 132 or
-// 656 B written per token.
+// Index rows: 16 lanes per token (four tokens per wave), each converting eight of the 128
+// values; the scale is the maximum over the token's 16 lanes.  Latent rows: one wave per
+// token, each lane converting eight of the 512 values; the 16 lanes of a 128-value group
+// reduce their maximum with xor shuffles, and lanes 0..15 copy the RoPE bytes.  Each lane
+// reads its eight source values with one 16-byte load (bf16) or two (fp32).  Both are
+// streams: 256 B (bf16 key) or 1,160 B (bf16 latent + RoPE) read and 132 or 656 B written
+// per token.
 //
 // Second layouts [same page, › FP8 潜在缓存: the uncompressed bf16 row and the per-tensor-scale
 // E4M3 row]: the bf16 row takes the latents rounded to nearest even and the RoPE bits as
@@ -35,8 +37,20 @@ constexpr float kE4m3Max = 448.0f;
 constexpr uint32_t kFaultSlot = 1u << 0;
 constexpr uint32_t kFaultRange = 1u << 4;
 
-__device__ __forceinline__ float load_value(const void* p, bool bf16, size_t i) {
-  return bf16 ? (float)static_cast<const __bf16*>(p)[i] : static_cast<const float*>(p)[i];
+// Eight consecutive source values (element i, a multiple of 8) as binary32, with one 16-byte
+// load for bf16 sources and two for fp32.
+template <typename T>
+__device__ __forceinline__ void load8(const void* p, size_t i, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  }
 }
 
 // Two binary32 values inside [-448, 448] -> two OCP E4M3 codes (round to nearest even) in
@@ -66,24 +80,42 @@ __device__ __forceinline__ int64_t dest_slot(const CacheWriteLaunch& a, int64_t 
   return slot;
 }
 
+// Index rows: 16 lanes per token (four tokens per wave), eight values per lane.
+constexpr int kIdxTokPerWg = kWavesPerWg * kWave / 16;
+template <typename T>
 __global__ __launch_bounds__(kWavesPerWg * kWave) void k_index_write(CacheWriteLaunch a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
-  if (token >= a.n_tokens) return;
+  const int l16 = threadIdx.x & 15;
+  const int64_t token = (int64_t)blockIdx.x * kIdxTokPerWg + (threadIdx.x >> 4);
+  if (token >= a.n_tokens) return;        // whole 16-lane groups leave together
   const int64_t slot = dest_slot(a, token);
   if (slot < 0) return;
-  const float x0 = load_value(a.src, a.bf16, token * 128 + 2 * lane);
-  const float x1 = load_value(a.src, a.bf16, token * 128 + 2 * lane + 1);
-  const bool finite = __builtin_isfinite(x0) && __builtin_isfinite(x1);
-  if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
-  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-  const float scale = amax / kE4m3Max;
-  const uint32_t codes = to_e4m3x2(quantise_input(x0, scale), quantise_input(x1, scale));
+  float x[8];
+  load8<T>(a.src, (size_t)token * 128 + 8 * l16, x);
+  bool finite = true;
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    finite &= __builtin_isfinite(x[e]);
+    m = fmaxf(m, fabsf(x[e]));
+  }
+  if (__any(!finite) && (threadIdx.x & (kWave - 1)) == 0) raise_fault(a.fault, kFaultRange);
+  // maximum over the token's 16 lanes
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+  const float scale = m / kE4m3Max;
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = to_e4m3x2(quantise_input(x[4 * h], scale), quantise_input(x[4 * h + 1], scale));
+    const uint32_t hi = to_e4m3x2(quantise_input(x[4 * h + 2], scale), quantise_input(x[4 * h + 3], scale));
+    w[h] = lo | (hi << 16);
+  }
   uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kIdxRowBytes;
-  *reinterpret_cast<uint16_t*>(row + 2 * lane) = (uint16_t)codes;
-  if (lane == 0) *reinterpret_cast<float*>(row + 128) = scale;
+  *reinterpret_cast<u32x2*>(row + 8 * l16) = u32x2{w[0], w[1]};
+  if (l16 == 0) *reinterpret_cast<float*>(row + 128) = scale;
 }
 
+template <typename T>
 __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write(CacheWriteLaunch a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
@@ -91,12 +123,10 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write(CacheWrite
   const int64_t slot = dest_slot(a, token);
   if (slot < 0) return;
   float x[8];
+  load8<T>(a.src, (size_t)token * 512 + 8 * lane, x);
   bool finite = true;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    x[e] = load_value(a.src, a.bf16, token * 512 + 8 * lane + e);
-    finite &= __builtin_isfinite(x[e]);
-  }
+  for (int e = 0; e < 8; ++e) finite &= __builtin_isfinite(x[e]);
   if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
   float m = 0.f;
 #pragma unroll
@@ -122,20 +152,21 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write(CacheWrite
   }
 }
 
+template <typename T>
 __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_bf16(CacheWriteLaunch a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
   if (token >= a.n_tokens) return;
   const int64_t slot = dest_slot(a, token);
   if (slot < 0) return;
+  float x[8];
+  load8<T>(a.src, (size_t)token * 512 + 8 * lane, x);
   uint32_t w[4];
   bool finite = true;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float x0 = load_value(a.src, a.bf16, token * 512 + 8 * lane + 2 * e);
-    const float x1 = load_value(a.src, a.bf16, token * 512 + 8 * lane + 2 * e + 1);
-    finite &= __builtin_isfinite(x0) && __builtin_isfinite(x1);
-    w[e] = bf16_bits(x0) | (bf16_bits(x1) << 16);
+    finite &= __builtin_isfinite(x[2 * e]) && __builtin_isfinite(x[2 * e + 1]);
+    w[e] = bf16_bits(x[2 * e]) | (bf16_bits(x[2 * e + 1]) << 16);
   }
   if (__any(!finite) && lane == 0) raise_fault(a.fault, kFaultRange);
   uint8_t* row = static_cast<uint8_t*>(a.pool) + slot * kBf16RowBytes;
@@ -147,6 +178,7 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_bf16(Cache
   }
 }
 
+template <typename T>
 __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_e4m3(CacheWriteLaunch a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t token = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
@@ -155,12 +187,10 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_e4m3(Cache
   if (slot < 0) return;
   const float scale = a.kv_scale;
   float x[8];
+  load8<T>(a.src, (size_t)token * 512 + 8 * lane, x);
   bool finite = true;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    x[e] = load_value(a.src, a.bf16, token * 512 + 8 * lane + e);
-    finite &= __builtin_isfinite(x[e]);
-  }
+  for (int e = 0; e < 8; ++e) finite &= __builtin_isfinite(x[e]);
   float r[4] = {0.f, 0.f, 0.f, 0.f};
   const bool has_rope = a.rope_dim && lane < 16;
   if (has_rope) {
@@ -187,20 +217,27 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_e4m3(Cache
   }
 }
 
+template <typename T>
+hipError_t launch_typed(const CacheWriteLaunch& a, hipStream_t st) {
+  constexpr int NT = kWavesPerWg * kWave;
+  const dim3 grid((unsigned)((a.n_tokens + kWavesPerWg - 1) / kWavesPerWg));
+  if (a.latent && a.bf16_rows)
+    k_latent_write_bf16<T><<<grid, NT, 0, st>>>(a);
+  else if (a.latent && a.e4m3_rows)
+    k_latent_write_e4m3<T><<<grid, NT, 0, st>>>(a);
+  else if (a.latent)
+    k_latent_write<T><<<grid, NT, 0, st>>>(a);
+  else
+    k_index_write<T><<<dim3((unsigned)((a.n_tokens + kIdxTokPerWg - 1) / kIdxTokPerWg)), NT, 0,
+                        st>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_cache_write(const CacheWriteLaunch& a, hipStream_t st) {
   if (a.n_tokens == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_tokens + kWavesPerWg - 1) / kWavesPerWg));
-  if (a.latent && a.bf16_rows)
-    k_latent_write_bf16<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
-  else if (a.latent && a.e4m3_rows)
-    k_latent_write_e4m3<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
-  else if (a.latent)
-    k_latent_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
-  else
-    k_index_write<<<grid, kWavesPerWg * kWave, 0, st>>>(a);
-  return hipGetLastError();
+  return a.bf16 ? launch_typed<__bf16>(a, st) : launch_typed<float>(a, st);
 }
 
 }  // namespace ml4

@@ -240,6 +240,11 @@ def test_cache_write_default_deny_lists_every_reason():
     rc = M.ml4_latent_cache_write(c2, 64, None, M.ML4_BF16, None, 64, 0, None, None, stream=0,
                                   check=False)
     assert rc == M.ML4_OK
+    # source rows are read as 16-byte vectors: an address off a 16-byte boundary is refused
+    # (host validation only: nothing is launched, the pointers are never dereferenced)
+    rc = M.ml4_index_cache_write(c2, 64, 4096 + 8, M.ML4_BF16, 5, 8192, None, stream=0,
+                                 check=False)
+    assert rc == M.ML4_E_INVALID and "16-byte aligned" in M.ml4_last_error()
 
 
 def test_second_layout_cache_writes_default_deny():
