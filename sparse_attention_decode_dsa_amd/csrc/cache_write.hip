@@ -194,9 +194,11 @@ __global__ __launch_bounds__(kWavesPerWg * kWave) void k_latent_write_e4m3(Cache
   float r[4] = {0.f, 0.f, 0.f, 0.f};
   const bool has_rope = a.rope_dim && lane < 16;
   if (has_rope) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(static_cast<const __bf16*>(a.rope) +
+                                                      (size_t)token * 64 + 4 * lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      r[e] = (float)static_cast<const __bf16*>(a.rope)[(size_t)token * 64 + 4 * lane + e];
+      r[e] = (float)v[e];
       finite &= __builtin_isfinite(r[e]);
     }
   }
