@@ -37,7 +37,8 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;   /* HIP's opaque stream handle */
 
-#define ML4_ABI_VERSION 5
+/* 6: the cache-write entries require 16-byte aligned source rows. */
+#define ML4_ABI_VERSION 6
 
 enum ml4_status {
   ML4_OK = 0,

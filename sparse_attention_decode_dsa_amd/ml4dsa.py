@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libml4dsa.so")
 
 # ---- constants mirrored from include/ml4dsa.h
-ML4_ABI_VERSION = 5
+ML4_ABI_VERSION = 6
 ML4_OK, ML4_E_INVALID, ML4_E_UNSUPPORTED, ML4_E_WORKSPACE, ML4_E_LAUNCH, ML4_E_DEVICE_FAULT = (
     0, -1, -2, -3, -4, -5)
 ML4_F32, ML4_BF16, ML4_FP8_E4M3 = 0, 1, 2
