@@ -33,7 +33,10 @@
 //           significant bits of P, which bounds the output error by 2^-11 * sum_t p_t |c_t|
 //           even when SSMax makes the softmax peaked.
 // One work-group barrier per tile: after QK the waves wait for the next tile's transfers,
-// so the barrier that publishes the partial S also publishes the next tile.
+// so the barrier that publishes the partial S also publishes the next tile.  With at most
+// 64 heads (the model's own head count, or a tensor-parallel share) half of those waves
+// would idle; there two wave groups take alternate tiles of the row instead, each with its
+// own softmax state, merged through LDS at the end (two barriers per step of two tiles).
 // A row's selected keys may be split across work-groups; the partial results are merged by
 // their log-sum-exp in a second kernel.
 #include "ml4_device.h"
@@ -108,7 +111,7 @@ __device__ __forceinline__ float sum_over_lane_groups(float v) {
 //                 bytes, never read) keeps rows off a 512-B LDS stride.
 constexpr int kFmtFp8 = 0, kFmtBf16 = 1, kFmtE4m3 = 2;
 
-template <int ROPE, int FMT>
+template <int ROPE, int FMT, bool TG = false>
 struct MlaGeom {
   static constexpr int ROW_BYTES =                                  // cache row stride
       FMT == kFmtFp8 ? 656 : FMT == kFmtBf16 ? 1152 : 576;
@@ -119,8 +122,10 @@ struct MlaGeom {
   // partial-S buffers, so that the barrier after QK also publishes the next tile.  The bf16 rows do not fit that and
   // keep two barriers per tile over a two-tile ring.
   static constexpr bool ONEBAR = FMT != kFmtBf16;
-  static constexpr int NSTAGE = ONEBAR ? 3 : 2;
-  static constexpr int XS_BUFS = ONEBAR ? 2 : 1;
+  // Two wave groups (at most 64 heads): four tile slots (two steps of two tiles), one
+  // exchange buffer.
+  static constexpr int NSTAGE = TG ? 4 : ONEBAR ? 3 : 2;
+  static constexpr int XS_BUFS = TG ? 1 : ONEBAR ? 2 : 1;
   static constexpr int RS = 16 * NCH;                   // bytes per gathered row
   static constexpr int RAW = kTK * NCH;                 // chunks per tile
   static constexpr int NBLK = (RAW + kWave - 1) / kWave;
@@ -135,6 +140,8 @@ struct MlaGeom {
   static constexpr int BYTES = OFF_MASK + (kMaxSplitKeys / kTK) * 4;
 };
 static_assert(MlaGeom<64, kFmtFp8>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<64, kFmtFp8, true>::BYTES <= 160 * 1024, "LDS budget");
+static_assert(MlaGeom<64, kFmtE4m3, true>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<64, kFmtBf16>::BYTES <= 160 * 1024, "LDS budget");
 static_assert(MlaGeom<0, kFmtFp8>::RS == 528 && MlaGeom<64, kFmtFp8>::RS == 656, "rows");
 static_assert(MlaGeom<0, kFmtBf16>::RS == 1024 && MlaGeom<64, kFmtBf16>::RS == 1152, "rows");
@@ -444,10 +451,11 @@ __device__ __forceinline__ void pv_tile(const unsigned char* raw, const float (&
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int ROPE, int FMT>
+template <int ROPE, int FMT, bool TG>
 __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit,
                                                          int keys_per_split, float* part) {
-  using G = MlaGeom<ROPE, FMT>;
+  using G = MlaGeom<ROPE, FMT, TG>;
+  static_assert(!TG || FMT != kFmtBf16, "two wave groups take the e4m3-coded rows");
   constexpr int NT = kMlaThreads;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   f32x4* xs = reinterpret_cast<f32x4*>(smem + G::OFF_XS);
@@ -460,10 +468,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int tid = threadIdx.x, tid0 = tid;
   const int lane0 = tid & (kWave - 1);
   const int wave = tid >> 6;
-  // Partners (same heads, other latent half) are waves 2 hg and 2 hg + 1; with fewer than
-  // 128 heads the idle head groups are the high ones, so the active waves spread over the
-  // four SIMDs (wave w runs on SIMD w % 4).
-  const int hg = wave >> 1, dh = wave & 1;
+  // Partners (same heads, other latent half) are waves 2 pair and 2 pair + 1.  One group:
+  // head group hg = pair; with fewer than 128 heads the idle head groups are the high ones,
+  // so the active waves spread over the four SIMDs (wave w runs on SIMD w % 4).  Two groups
+  // (TG, at most 64 heads): waves 4 grp .. 4 grp + 3, head group hg = pair & 1.
+  const int pair = wave >> 1, dh = wave & 1;
+  const int grp = TG ? wave >> 2 : 0;
+  const int hg = TG ? pair & 1 : pair;
   const int r = blockIdx.x;
   const int hbase = blockIdx.y * kHeadsPerWg;
   const int h0 = hbase + hg * 32;
@@ -649,37 +660,25 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   float l_part[2] = {0.f, 0.f};
   bool sc_bad = false;   // a latent scale that could push P * scale out of fp16
 
-  if constexpr (G::ONEBAR) {
-    if (ntiles > 0) issue(0, lane0);
-    if (ntiles > 1) issue(1, lane0);
-    if (ntiles > 1) wait_vmcnt<G::PER_WAVE>();
-    else wait_vmcnt<0>();
-    __syncthreads();   // tile 0 is in LDS
-  } else {
-#pragma unroll
-    for (int t = 0; t < G::NSTAGE - 1; ++t)
-      if (t < ntiles) issue(t, lane0);
-  }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    // Lane-derived addresses are recomputed every tile (a few VALU instructions) rather than
-    // hoisted out of the loop: the query and the accumulator leave no registers to keep them.
+  // One tile's phases.  Lane-derived addresses are recomputed every tile (a few VALU
+  // instructions) rather than hoisted out of the loop: the query and the accumulator leave
+  // no registers to keep them.
+  auto opaque_lane = [&]() {
     int lane = lane0;
     asm volatile("" : "+v"(lane));
+    return lane;
+  };
+  auto tile_raw = [&](int tile) {
+    return smem + (tile % G::NSTAGE) * G::STAGE;
+  };
+  // QK: this wave's partial S^T of the tile into its exchange slot.
+  auto do_qk = [&](int tile, f32x4* xsb) {
+    const int lane = opaque_lane();
     const int g16 = lane >> 4, c16 = lane & 15;
-    const unsigned char* raw = smem + (tile % G::NSTAGE) * G::STAGE;
-    if constexpr (!G::ONEBAR) {
-      // Two-tile ring: this tile's transfers are the only outstanding ones.
-      static_assert(G::NSTAGE == 2, "the wait below assumes one tile in flight");
-      wait_vmcnt<0>();
-      __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
-      if (tile + G::NSTAGE - 1 < ntiles) issue(tile + G::NSTAGE - 1, lane);
-    }
-    f32x4* xsb = xs + (G::ONEBAR ? (tile & 1) * G::XS_WORDS : 0);
-
-    // ---- partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
-    //      partner waves then add half 0 + half 1 in the same order.  Waves whose heads are
-    //      all past n_heads only move data and keep the barriers.
-    if (active) {
+    const unsigned char* raw = tile_raw(tile);
+    // Partial S^T over this wave's dims per key sub-tile, exchanged through LDS; both
+    // partner waves then add half 0 + half 1 in the same order.
+    {
       const __bf16* qr_lane = qr_sh + (hg * 32 + c16) * kQRS + 32 * dh + 8 * g16;
       f32x4* mine = xsb + wave * 4 * kWave;
       if constexpr (FMT == kFmtFp8) {
@@ -696,13 +695,19 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       }
       }
     }
+  };
+  // Softmax and PV of the tile, from both halves' partial S in the exchange buffer.
+  auto do_smpv = [&](int tile, const f32x4* xsb) {
+    const int lane = opaque_lane();
+    const int g16 = lane >> 4, c16 = lane & 15;
+    const unsigned char* raw = tile_raw(tile);
     // Both halves' partial S of this wave's heads and the tile's key mask, read after the
     // barrier.  (Reading them before the gather of tile + 2 is issued spills.)
     f32x4 ps0[2][2], ps1[2][2];
     uint32_t vmask = 0;
     auto load_partials = [&]() {
-      const f32x4* p0 = xsb + (2 * hg) * 4 * kWave;
-      const f32x4* p1 = xsb + (2 * hg + 1) * 4 * kWave;
+      const f32x4* p0 = xsb + (2 * pair) * 4 * kWave;
+      const f32x4* p1 = xsb + (2 * pair + 1) * 4 * kWave;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -712,19 +717,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
         }
       vmask = mask_sh[tile];
     };
-    if constexpr (G::ONEBAR) {
-      // Only tile + 1's transfers are outstanding.  After the barrier every wave's partial
-      // S of this tile and tile + 1 are in LDS, and every wave is done with tile - 1, whose
-      // ring slot takes tile + 2.
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (tile + 2 < ntiles) issue(tile + 2, lane);
-      if (active) load_partials();
-    } else {
-      __syncthreads();
-      if (active) load_partials();
-    }
-    if (!active) continue;
+    load_partials();
     // Logits: half 0 + half 1 in the same order in both partners.  With a positive logit
     // scale c (every format but plain E4M3, whose per-head query scale may take any sign) c
     // is applied inside the exponent's fma and the tile maximum is max(s) * c; otherwise the
@@ -814,9 +807,102 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
       if (dh == 0) pv_tile<ROPE, FMT, 0>(raw, pv, o_acc, sc_bad, g16, c16);
       else pv_tile<ROPE, FMT, 1>(raw, pv, o_acc, sc_bad, g16, c16);
     }
+  };
+
+  if constexpr (TG) {
+    // Two wave groups over one set of at most 64 heads: waves 0-3 take the even tiles,
+    // waves 4-7 the odd ones, each group with its own softmax state, merged at the end.
+    // Per step two tiles: [wait for them, barrier, gather the next two] [QK] [barrier]
+    // [softmax, PV].  The ring holds two steps (four tile slots); one exchange buffer,
+    // the groups on disjoint wave slots.
+    for (int t = 0; t < 2; ++t)
+      if (t < ntiles) issue(t, lane0);
+    const int nsteps = (ntiles + 1) / 2;
+    for (int st = 0; st < nsteps; ++st) {
+      const int tile = __builtin_amdgcn_readfirstlane(2 * st + grp);   // wave-uniform
+      const bool mine_ok = active && tile < ntiles;
+      wait_vmcnt<0>();
+      __syncthreads();   // this step's tiles are in LDS; every wave is done with the last
+      for (int t = 2 * st + 2; t < 2 * st + 4; ++t)
+        if (t < ntiles) issue(t, opaque_lane());
+      if (mine_ok) do_qk(tile, xs);
+      __syncthreads();   // partial S published
+      if (mine_ok) do_smpv(tile, xs);
+    }
+  } else {
+  if constexpr (G::ONEBAR) {
+    if (ntiles > 0) issue(0, lane0);
+    if (ntiles > 1) issue(1, lane0);
+    if (ntiles > 1) wait_vmcnt<G::PER_WAVE>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // tile 0 is in LDS
+  } else {
+#pragma unroll
+    for (int t = 0; t < G::NSTAGE - 1; ++t)
+      if (t < ntiles) issue(t, lane0);
+  }
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if constexpr (!G::ONEBAR) {
+      // Two-tile ring: this tile's transfers are the only outstanding ones.
+      static_assert(G::NSTAGE == 2, "the wait below assumes one tile in flight");
+      wait_vmcnt<0>();
+      __syncthreads();   // the tile is in LDS; every wave is done with the previous tile
+      if (tile + G::NSTAGE - 1 < ntiles) issue(tile + G::NSTAGE - 1, opaque_lane());
+    }
+    f32x4* xsb = xs + (G::ONEBAR ? (tile & 1) * G::XS_WORDS : 0);
+    // Waves whose heads are all past n_heads only move data and keep the barriers.
+    if (active) do_qk(tile, xsb);
+    if constexpr (G::ONEBAR) {
+      // Only tile + 1's transfers are outstanding.  After the barrier every wave's partial
+      // S of this tile and tile + 1 are in LDS, and every wave is done with tile - 1, whose
+      // ring slot takes tile + 2.
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tile + 2 < ntiles) issue(tile + 2, opaque_lane());
+    } else {
+      __syncthreads();
+    }
+    if (active) do_smpv(tile, xsb);
+  }
   }
 
   if (__any(sc_bad) && lane0 == 0) raise_fault(a.fault, kFaultRange);
+
+  if constexpr (TG) {
+    // Group 1's softmax state (running maximum, partial sums, accumulator) through LDS to
+    // its group-0 counterpart (same heads, same dims, same lane layout), which rescales
+    // both to the larger maximum and adds them; one head tile at a time.
+    constexpr int kItems = 2 + 16 * 4;
+    static_assert(4 * kItems * kWave * 4 <= G::BYTES, "merge area");
+    float* mg = reinterpret_cast<float*>(smem) + (wave & 3) * kItems * kWave + lane0;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      __syncthreads();   // every wave is done with the ring / the previous head tile
+      if (grp == 1 && active) {
+        mg[0] = m_run[ht];
+        mg[kWave] = l_part[ht];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mg[(2 + 4 * i + j) * kWave] = o_acc[ht][i][j];
+      }
+      __syncthreads();
+      if (grp == 0 && active) {
+        const float m1 = mg[0], l1 = mg[kWave];
+        const float M = fmaxf(m_run[ht], m1);
+        const float a0 = m_run[ht] == -__builtin_inff() ? 0.f : exp2f(m_run[ht] - M);
+        const float a1 = m1 == -__builtin_inff() ? 0.f : exp2f(m1 - M);
+        l_part[ht] = l_part[ht] * a0 + l1 * a1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o_acc[ht][i][j] = o_acc[ht][i][j] * a0 + mg[(2 + 4 * i + j) * kWave] * a1;
+        m_run[ht] = M;
+      }
+    }
+    if (grp == 1) return;
+  }
 
   // ---- epilogue: lane (g, i) holds O[head h0 + 16 ht + i][dims 256 dh + 16 t + 4 g + j]
   if (!active) return;
@@ -854,9 +940,9 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   (void)c16;
 }
 
-template <int ROPE, int FMT>
+template <int ROPE, int FMT, bool TG>
 constexpr size_t mla_lds_bytes() {
-  return (size_t)MlaGeom<ROPE, FMT>::BYTES;
+  return (size_t)MlaGeom<ROPE, FMT, TG>::BYTES;
 }
 
 // Merge split partials: o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) (base-2 lse).
@@ -1016,19 +1102,31 @@ MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
   return pl;
 }
 
-template <int ROPE, int FMT>
-hipError_t launch_rows(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
-  constexpr size_t lds = mla_lds_bytes<ROPE, FMT>();
+template <int ROPE, int FMT, bool TG>
+hipError_t launch_rows_tg(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
+  constexpr size_t lds = mla_lds_bytes<ROPE, FMT, TG>();
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8<ROPE, FMT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8<ROPE, FMT, TG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   dim3 grid(a.s.total_q, pl.groups, pl.nsplit);
-  k_mla_fp8<ROPE, FMT><<<grid, kMlaThreads, lds, st>>>(a, pl.nsplit, pl.keys_per_split, part);
+  k_mla_fp8<ROPE, FMT, TG><<<grid, kMlaThreads, lds, st>>>(a, pl.nsplit, pl.keys_per_split,
+                                                           part);
   return hipGetLastError();
+}
+
+// At most 64 heads use half the waves of a 128-head work-group; two wave groups then take
+// alternate tiles of the row (measured at 64 / 16 heads on the 64k verify selections:
+// 171.8 -> 135.0 us / 150.8 -> 118.5 us).
+template <int ROPE, int FMT>
+hipError_t launch_rows(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
+  if constexpr (FMT != kFmtBf16) {
+    if (a.n_heads <= 64) return launch_rows_tg<ROPE, FMT, true>(a, pl, part, st);
+  }
+  return launch_rows_tg<ROPE, FMT, false>(a, pl, part, st);
 }
 
 }  // namespace
