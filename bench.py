@@ -634,7 +634,10 @@ def main():
             roof["kernel"] = {"indexer": "k_indexer_f32", "mla": "k_mla_f32",
                               "topk": "k_topk_cand"}[dom]
         else:
-            roof["kernel"] = {"indexer": "k_indexer_fp8", "mla": "k_mla_fp8<%d, 0>" % rope0,
+            # k_mla_fp8<rope, format, two wave groups (<= 64 heads)>
+            roof["kernel"] = {"indexer": "k_indexer_fp8",
+                              "mla": "k_mla_fp8<%d, 0, %s>" % (
+                                  rope0, "true" if case.mla_heads <= 64 else "false"),
                               "topk": "k_topk_cand"}[dom]
         roof["layer"] = l0
         roof["avg_launch_us"] = us
