@@ -476,7 +476,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   const int grp = TG ? wave >> 2 : 0;
   const int hg = TG ? pair & 1 : pair;
   const int r = blockIdx.x;
-  const int hbase = blockIdx.y * kHeadsPerWg;
+  constexpr int HPW = TG ? 64 : kHeadsPerWg;   // heads per work-group
+  const int hbase = blockIdx.y * HPW;
   const int h0 = hbase + hg * 32;
   const int split = blockIdx.z;
   const SeqView& s = a.s;
@@ -553,7 +554,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_fp8(MlaLaunch a, int nsplit
   if (bad_b) raise_fault(a.fault, kFaultBlock);
   // RoPE query of the group's heads (bf16, as given) into LDS.
   if (ROPE && FMT != kFmtE4m3) {
-    for (int i = tid; i < kHeadsPerWg * 8; i += NT) {
+    for (int i = tid; i < HPW * 8; i += NT) {
       const int hh = i >> 3, q8 = i & 7;
       u32x4 v = u32x4{0, 0, 0, 0};
       if (hbase + hh < H)
@@ -1085,9 +1086,10 @@ struct MlaPlan {
 
 // One work-group per (row, 128 heads, key split); splits only when the grid would leave
 // CUs idle.
-MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
+MlaPlan plan_mla(const SeqView& s, int H, int top_k, bool tg) {
   MlaPlan pl{};
-  pl.groups = (H + kHeadsPerWg - 1) / kHeadsPerWg;
+  const int hpw = tg ? 64 : kHeadsPerWg;
+  pl.groups = (H + hpw - 1) / hpw;
   const long long base = (long long)s.total_q * pl.groups;
   // >= 4 tiles per split: below that the partials (2 KB per row, head and split, written
   // and read back) and each split's copy of the row's queries outweigh the extra CUs
@@ -1100,6 +1102,17 @@ MlaPlan plan_mla(const SeqView& s, int H, int top_k) {
   const int per = (top_k + ns - 1) / ns;
   pl.keys_per_split = (per + kTK - 1) / kTK * kTK;
   return pl;
+}
+
+// The two-wave-group form (64 heads per work-group) serves at most 64 heads, and more heads
+// whenever 128-head work-groups would leave CUs idle (few decode rows): each row then takes
+// twice the work-groups, with every wave busy (8 decode rows at 32k: 41.9 -> 37.6 us; one
+// row at 1M positions: 35.5 -> 29.7 us).  Rows of bf16 cache lines keep one group.
+bool use_two_groups(const SeqView& s, int H, int top_k, bool bf16_rows) {
+  if (bf16_rows) return false;
+  if (H <= 64) return true;
+  const MlaPlan one = plan_mla(s, H, top_k, false);
+  return (long long)s.total_q * one.groups * one.nsplit < 256;
 }
 
 template <int ROPE, int FMT, bool TG>
@@ -1122,19 +1135,22 @@ hipError_t launch_rows_tg(const MlaLaunch& a, const MlaPlan& pl, float* part, hi
 // alternate tiles of the row (measured at 64 / 16 heads on the 64k verify selections:
 // 171.8 -> 135.0 us / 150.8 -> 118.5 us).
 template <int ROPE, int FMT>
-hipError_t launch_rows(const MlaLaunch& a, const MlaPlan& pl, float* part, hipStream_t st) {
+hipError_t launch_rows(const MlaLaunch& a, bool tg, const MlaPlan& pl, float* part,
+                       hipStream_t st) {
   if constexpr (FMT != kFmtBf16) {
-    if (a.n_heads <= 64) return launch_rows_tg<ROPE, FMT, true>(a, pl, part, st);
+    if (tg) return launch_rows_tg<ROPE, FMT, true>(a, pl, part, st);
   }
   return launch_rows_tg<ROPE, FMT, false>(a, pl, part, st);
 }
 
 }  // namespace
 
+// Enough for either work-group form (the row format is not an argument here).
 size_t mla_ws_bytes(const SeqView& s, int n_heads, int top_k) {
-  const MlaPlan pl = plan_mla(s, n_heads, top_k);
-  if (pl.nsplit <= 1) return 0;
-  return align_up((size_t)s.total_q * n_heads * pl.nsplit * 513 * sizeof(float), 256);
+  const int ns = max(plan_mla(s, n_heads, top_k, false).nsplit,
+                     plan_mla(s, n_heads, top_k, true).nsplit);
+  if (ns <= 1) return 0;
+  return align_up((size_t)s.total_q * n_heads * ns * 513 * sizeof(float), 256);
 }
 
 hipError_t launch_mla(const MlaLaunch& a, hipStream_t st) {
@@ -1142,18 +1158,19 @@ hipError_t launch_mla(const MlaLaunch& a, hipStream_t st) {
     k_mla_f32<<<dim3(a.s.total_q, a.n_heads), 256, 0, st>>>(a);
     return hipGetLastError();
   }
-  const MlaPlan pl = plan_mla(a.s, a.n_heads, a.top_k);
+  const bool tg = use_two_groups(a.s, a.n_heads, a.top_k, a.bf16_rows);
+  const MlaPlan pl = plan_mla(a.s, a.n_heads, a.top_k, tg);
   float* part = pl.nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
   hipError_t e;
   if (a.bf16_rows)
-    e = a.rope_dim ? launch_rows<64, kFmtBf16>(a, pl, part, st)
-                   : launch_rows<0, kFmtBf16>(a, pl, part, st);
+    e = a.rope_dim ? launch_rows<64, kFmtBf16>(a, false, pl, part, st)
+                   : launch_rows<0, kFmtBf16>(a, false, pl, part, st);
   else if (a.e4m3_rows)
-    e = a.rope_dim ? launch_rows<64, kFmtE4m3>(a, pl, part, st)
-                   : launch_rows<0, kFmtE4m3>(a, pl, part, st);
+    e = a.rope_dim ? launch_rows<64, kFmtE4m3>(a, tg, pl, part, st)
+                   : launch_rows<0, kFmtE4m3>(a, tg, pl, part, st);
   else
-    e = a.rope_dim ? launch_rows<64, kFmtFp8>(a, pl, part, st)
-                   : launch_rows<0, kFmtFp8>(a, pl, part, st);
+    e = a.rope_dim ? launch_rows<64, kFmtFp8>(a, tg, pl, part, st)
+                   : launch_rows<0, kFmtFp8>(a, tg, pl, part, st);
   if (e != hipSuccess || pl.nsplit <= 1) return e;
   k_mla_combine<<<dim3(a.s.total_q, a.n_heads), 128, 0, st>>>(a, pl.nsplit, part);
   return hipGetLastError();
