@@ -947,45 +947,56 @@ constexpr size_t mla_lds_bytes() {
 }
 
 // Merge split partials: o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) (base-2 lse).
-// The splits' lse values are read once into LDS (one load per thread, all in flight) and
-// the partial outputs four splits at a time, so a merge costs a few memory round trips
-// whatever the number of splits.
+// The partial outputs of the first kMergeAhead splits are loaded before their weights are
+// known, together with every split's lse (one memory round trip for the usual split
+// counts); the weights are taken one split per lane, their sum and the weighted sum in
+// split order.
 constexpr int kMaxSplits = (kMaxSplitKeys + kTK - 1) / kTK;
+constexpr int kMergeAhead = 16;
+static_assert(kMaxSplits <= kWave, "one split per lane of the first wave");
 __global__ __launch_bounds__(128) void k_mla_combine(MlaLaunch a, int nsplit, const float* part) {
   __shared__ float wsh[kMaxSplits];
   __shared__ float Msh, Lsh;
   const int r = blockIdx.x, h = blockIdx.y;
   const int H = a.n_heads;
   const float* base = part + ((size_t)r * H + h) * nsplit * 513;
-  for (int sp = threadIdx.x; sp < nsplit; sp += 128) wsh[sp] = base[sp * 513 + 512];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -__builtin_inff();
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wsh[sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float wgt = wsh[sp] == -__builtin_inff() ? 0.f : exp2f(wsh[sp] - M);
-      wsh[sp] = wgt;
-      L += wgt;
-    }
-    Msh = M;
-    Lsh = L;
+  const int d = 4 * threadIdx.x;
+  f32x4 v[kMergeAhead];
+#pragma unroll
+  for (int u = 0; u < kMergeAhead; ++u) {
+    const float* o = base + u * 513 + d;
+    v[u] = u < nsplit ? f32x4{o[0], o[1], o[2], o[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (threadIdx.x < kWave) {
+    const int sp = threadIdx.x;
+    const float l = sp < nsplit ? base[sp * 513 + 512] : -__builtin_inff();
+    const float M = wave_max(l);
+    if (sp < nsplit) wsh[sp] = l == -__builtin_inff() ? 0.f : exp2f(l - M);
+    if (sp == 0) Msh = M;
   }
   __syncthreads();
-  const float M = Msh, L = Lsh;
-  const int d = 4 * threadIdx.x;
+  if (threadIdx.x == 0) {
+    float L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) L += wsh[sp];
+    Lsh = L;
+  }
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
-    f32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < kMergeAhead; ++u)
+    if (u < nsplit) acc += wsh[u] * v[u];
+  for (int sp0 = kMergeAhead; sp0 < nsplit; sp0 += 4) {
+    f32x4 w[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float* o = base + (sp0 + u) * 513 + d;
-      v[u] = sp0 + u < nsplit ? f32x4{o[0], o[1], o[2], o[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+      w[u] = sp0 + u < nsplit ? f32x4{o[0], o[1], o[2], o[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (sp0 + u < nsplit) acc += wsh[sp0 + u] * v[u];
+      if (sp0 + u < nsplit) acc += wsh[sp0 + u] * w[u];
   }
+  __syncthreads();
+  const float M = Msh, L = Lsh;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   acc *= inv;
   __bf16* out = static_cast<__bf16*>(a.out) + ((size_t)r * H + h) * 512 + d;
