@@ -283,7 +283,8 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
  *   Arguments, results, validation and fault bits as ml4_sparse_attn_layer.
  *   A batch whose ml4_workspace_bytes(ML4_ENTRY_LAYER, ...) exceeds ML4_STATIC_SCRATCH_BYTES
  *   is refused with ML4_E_UNSUPPORTED (nothing launched); 64 MiB holds the scores of
- *   256 query rows at 65,536 positions or of one row at up to 16M positions.
+ *   256 query rows at 65,536 positions, or the scores and top-k lists (12 bytes per
+ *   position) of one row at up to 4M positions.
  *   Every call on one GPU uses that GPU's one array: calls that may overlap in time on the
  *   same GPU (other streams, other host threads) race and must be ordered by the caller.
  */

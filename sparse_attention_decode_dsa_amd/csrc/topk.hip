@@ -17,10 +17,9 @@
 // threshold taken from a sample (one read of the row), and run steps 2-3 on that list; the
 // streaming form above is their fallback when the list misses.  Rows up to 32,768 positions
 // hold the whole row in registers (32 keys per thread), so the sample and the candidate
-// pass read no memory.  Longer rows use a
-// multi-work-group version with the same steps, one launch per pass over the row, its
-// histograms merged with integer atomics; each work-group of a pass redoes the per-row
-// digit pick from the previous pass's histogram, so no launch is spent on it.
+// pass read no memory.  Longer rows take two launches: many work-groups per row
+// filter their chunks against the sampled threshold into per-chunk lists, then one
+// work-group per row selects from the concatenated lists.
 #include "ml4_device.h"
 
 namespace ml4 {
@@ -81,19 +80,29 @@ __device__ int block_exclusive_scan(int v, int* total, int* sh) {
 }
 
 // Given a histogram (nb bins, descending order of digit = descending key), find the digit d
-// with above(d) < need <= above(d) + hist[d].  Writes {d, above(d), hist[d]} to out.
+// with above(d) < need <= above(d) + hist[d].  Writes {d, above(d), hist[d]} to out.  Thread
+// i scans the digits nb-1-B i .. nb-B-B i (B = 2,048 / NT) in descending order.
 template <int NT>
 __device__ void find_digit(const uint32_t* hist, int nb, int need, int* out, int* sh) {
-  const int i0 = 2 * threadIdx.x;
-  const int d1 = nb - 1 - i0, d0 = nb - 2 - i0;
-  const int c1 = d1 >= 0 ? (int)hist[d1] : 0;
-  const int c0 = d0 >= 0 ? (int)hist[d0] : 0;
+  constexpr int B = (1 << kMaxDigitBits) / NT;
+  static_assert(B >= 1 && B * NT == (1 << kMaxDigitBits), "whole digits per thread");
+  int c[B];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int d = nb - 1 - (B * (int)threadIdx.x + j);
+    c[j] = d >= 0 ? (int)hist[d] : 0;
+    sum += c[j];
+  }
   int total;
-  const int ex = block_exclusive_scan<NT>(c1 + c0, &total, sh);
-  if (d1 >= 0 && ex < need && need <= ex + c1) {
-    out[0] = d1; out[1] = ex; out[2] = c1;
-  } else if (d0 >= 0 && ex + c1 < need && need <= ex + c1 + c0) {
-    out[0] = d0; out[1] = ex + c1; out[2] = c0;
+  int ex = block_exclusive_scan<NT>(sum, &total, sh);
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int d = nb - 1 - (B * (int)threadIdx.x + j);
+    if (d >= 0 && ex < need && need <= ex + c[j]) {
+      out[0] = d; out[1] = ex; out[2] = c[j];
+    }
+    ex += c[j];
   }
   __syncthreads();
 }
@@ -361,6 +370,7 @@ constexpr int kSampleVec = 1024;
 // With stop_shift > 0 the search ends once the bits above stop_shift are known and the
 // result has its low stop_shift bits cleared (a lower bound of that key; *above is then
 // not meaningful).
+template <int NT = kRowThreads>
 __device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above_out,
                                uint32_t* hist, int* sh_scan, int* sh_sel, int stop_shift = 0) {
   uint32_t P = 0;        // bits of the answer above `shift`
@@ -369,14 +379,14 @@ __device__ uint32_t lds_select(const uint32_t* keys, int m, int rank, int* above
     const int w = min(kMaxDigitBits, shift);
     const int nsh = shift - w;
     const int nb = 1 << w;
-    for (int i = threadIdx.x; i < nb; i += kRowThreads) hist[i] = 0u;
+    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < m; i += kRowThreads) {
+    for (int i = threadIdx.x; i < m; i += NT) {
       const uint32_t k = keys[i];
       if (digit_prefix(k, shift) == P) atomicAdd(&hist[(k >> nsh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    find_digit<NT>(hist, nb, need, sh_sel, sh_scan);
     const int d = sh_sel[0], above = sh_sel[1];
     __syncthreads();
     P = (uint32_t)((P << w) | (uint32_t)d);
@@ -679,352 +689,290 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
                               sh_sel);
 }
 
-// ------------------------------------------------------------------ many work-groups per row
-// Per-row selection state of the multi-work-group path.  The rule being refined is
-// "keep key if key >> shift > P; keep it if key >> shift == P and it is among the first
-// `need` such keys in t order"; `resolved` stops refinement once a bucket is taken whole.
-// Slot p of a row holds the state S_p that pass p used (written by the pass's first
-// work-group, read by the next launch); the AND/OR pass leaves one (AND, OR, NaN) triple
-// per chunk, which pass 0 reduces.  Every
-// work-group of a pass derives S_p itself from S_{p-1} and the histogram of pass p - 1, so
-// no launch is spent on the per-row step and no work-group waits for another.
-struct alignas(16) BigState {
-  uint32_t and_v, or_v, nan, active;
-  uint64_t P;
-  int shift, need;
-  int resolved, pad0, pad1, pad2;
-};
+// ------------------------------------------------- long rows: chunk filters, then one select
+// Rows above 131,072 positions, two launches.
+// 1. k_tkl_filter, one work-group per 16,384-position chunk of a row: every work-group of the
+//    row takes the same threshold T from the same 8,192-key sample (the candidate filter's
+//    rule, here rank ~1.5 K n_s / n + 16 to 22 leading bits, and T >= 1 so that NaN never
+//    passes), then writes the chunk's keys >= T with their positions, in position order, to
+//    the chunk's own list, and the list's length.
+// 2. k_tkl_select, one work-group per row: the chunk lists taken in chunk order are the row's
+//    keys >= T in position order.  With at least K and at most kLongCand of them, the top K
+//    of the row are the top K of the list: thread i holds entries 16 i .. 16 i + 15 in
+//    registers, radix passes below the list's common leading bits give the K-th key, and two
+//    block scans place the kept positions in ascending order, keys equal to the K-th lowest
+//    position first.  A list that misses takes the streaming exact selection.
+constexpr int kLongEpt = 16;                          // keys per thread in both launches
+constexpr int kLongChunk = kLongEpt * kRowThreads;    // 16,384 positions per filter work-group
+constexpr int kLongCand = kLongEpt * kRowThreads;     // longest list the select holds
+constexpr int kLongSample = 8192;                     // sample keys: two float4 per thread
+constexpr int kMaxLongChunks = kRowThreads;           // one chunk length per select thread
 
-constexpr int kBigSlots = 4;      // S_0 .. S_3
-constexpr int kBigPasses = 3;     // 3 x 11 digit bits >= 32
-constexpr int kHistBins = 1 << kMaxDigitBits;
-
-struct BigWs {
-  BigState* st;    // [rows][kBigSlots]
-  uint32_t* hist;  // [rows][kBigPasses][2048], one histogram per pass
-  int* cnt;        // [rows][chunks][2]  keys above / equal to the final threshold
-  u32x4* ao;       // [rows][chunks]     AND, OR, NaN flag of the chunk's keys
-  int chunks;
+struct LongWs {
+  int* cnt;      // [rows][chunks]              length of each chunk's list
+  u32x2* list;   // [rows][chunks][kLongChunk]  (key, position), position order
 };
 
 __host__ __device__ __forceinline__ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__device__ __forceinline__ BigWs big_ws(void* ws, int rows, int chunks) {
-  BigWs w;
+__device__ __forceinline__ LongWs long_ws(void* ws, int rows, int chunks) {
   char* p = static_cast<char*>(ws);
-  w.st = reinterpret_cast<BigState*>(p);
-  p += round256((size_t)rows * kBigSlots * sizeof(BigState));
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += round256((size_t)rows * kBigPasses * kHistBins * 4);
+  LongWs w;
   w.cnt = reinterpret_cast<int*>(p);
-  p += round256((size_t)rows * chunks * 2 * sizeof(int));
-  w.ao = reinterpret_cast<u32x4*>(p);
-  w.chunks = chunks;
+  w.list = reinterpret_cast<u32x2*>(p + round256((size_t)rows * chunks * sizeof(int)));
   return w;
 }
 
-// Keys lo + 16 i .. lo + 16 i + 15 of the row into thread i's registers, four 16-byte loads
-// in flight at once (a chunk is kBigThreads x 16 keys); bit e of *valid marks key e < hi.
-static_assert(kBigChunk == 16 * kBigThreads, "one 16-key run per thread");
-__device__ __forceinline__ void load_run16(const float* row, int lo, int hi, uint32_t (&k)[16],
-                                           uint32_t* valid, bool* any_nan) {
-  const int t0 = lo + 16 * (int)threadIdx.x;
-  f32x4 v[4];
+__global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int chunks) {
+  constexpr int NW = kRowThreads / kWave;
+  constexpr int SV = kLongSample / 4 / kRowThreads;   // sample float4 per thread
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ int sh_scan[NW];
+  __shared__ int sh_sel[4];
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
+  const int r = blockIdx.x, c = blockIdx.y;
+  int n = 0;
+  if (row_kind(a, r, &n) != 0) return;   // the select launch writes such rows
+  const int lo = c * kLongChunk, hi = min(n, lo + kLongChunk);
+  if (lo >= hi) return;                  // past this row's end: the select reads no list here
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const float* row = a.scores + (size_t)r * a.ld;
+  const int n4 = (n + 3) >> 2;
+  // The chunk's 16 keys per thread and the sample's vectors, all loads in flight at once.
+  // Rows are 16-byte aligned with ld >= 4 n4, so every vector read lies inside the row.
+  const int t0 = lo + kLongEpt * tid;
+  f32x4 v[kLongEpt / 4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)   // t0 + 4j < hi <= ld, a multiple of 4: the whole vector is in the row
+  for (int j = 0; j < kLongEpt / 4; ++j)
     v[j] = t0 + 4 * j < hi ? *reinterpret_cast<const f32x4*>(row + t0 + 4 * j)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
-  uint32_t ok = 0u;
-  bool nan = false;
+  int si[SV];
+  f32x4 sv[SV];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    bool nn = false;
-    k[e] = order_key(v[e >> 2][e & 3], nn);
-    if (t0 + e < hi) {
-      ok |= 1u << e;
-      nan |= nn;
-    }
+  for (int u = 0; u < SV; ++u) {
+    const int j = tid + kRowThreads * u;
+    si[u] = (int)(((long long)j * n4) / (kLongSample / 4));
+    sv[u] = *reinterpret_cast<const f32x4*>(row + 4 * si[u]);
   }
-  *valid = ok;
-  *any_nan = nan;
-}
-
-__device__ __forceinline__ bool refining(const BigState& s) {
-  return s.active && s.shift > 0 && !s.resolved;
-}
-
-// S_p from S_{p-1} and pass p-1's histogram g (a kBigThreads work-group, every thread calls
-// it): the digit of the need-th key, thread i taking the 8 digits nb-1-8i .. nb-8-8i in
-// descending order.  A finished state is returned as it is.
-__device__ BigState pick_digit(const BigState& s, const uint32_t* g, int* sh_scan, int* sh_sel) {
-  if (!refining(s)) return s;
-  const int wd = min(kMaxDigitBits, s.shift), nb = 1 << wd;
-  constexpr int kBpt = kHistBins / kBigThreads;
-  uint32_t c[kBpt];
-  int sum = 0;
-#pragma unroll
-  for (int j = 0; j < kBpt; ++j) {
-    const int d = nb - 1 - (kBpt * (int)threadIdx.x + j);
-    c[j] = d >= 0 ? g[d] : 0u;
-    sum += (int)c[j];
-  }
-  int total;
-  int ex = block_exclusive_scan<kBigThreads>(sum, &total, sh_scan);
-#pragma unroll
-  for (int j = 0; j < kBpt; ++j) {
-    const int d = nb - 1 - (kBpt * (int)threadIdx.x + j);
-    if (d >= 0 && ex < s.need && s.need <= ex + (int)c[j]) {
-      sh_sel[0] = d; sh_sel[1] = ex; sh_sel[2] = (int)c[j];
-    }
-    ex += (int)c[j];
-  }
-  __syncthreads();
-  BigState o = s;
-  o.P = (s.P << wd) | (uint64_t)sh_sel[0];
-  o.need = s.need - sh_sel[1];
-  o.shift = s.shift - wd;
-  o.resolved = (sh_sel[2] == o.need) ? 1 : 0;
-  __syncthreads();   // sh_sel is reused by the caller
-  return o;
-}
-
-// AND/OR of each chunk's keys (the leading bits common to the row are skipped by pass 0).
-// Work-group 0 of each row also writes the output of a row that needs no selection and
-// clears the row's per-pass histograms.
-__global__ __launch_bounds__(kBigThreads) void k_tkb_andor(TopkLaunch a, int chunks) {
-  const int r = blockIdx.y;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  int n = 0;
-  if (row_kind(a, r, &n) != 0) {
-    if (blockIdx.x == 0) {
-      row_prologue(a, r, &n);
-      if (threadIdx.x < kBigSlots) {
-        const BigState idle{~0u, 0u, 0u, 0u, 0ull, 0, 0, 0, 0, 0, 0};
-        w.st[(size_t)r * kBigSlots + threadIdx.x] = idle;
-      }
-    }
-    return;
-  }
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < kBigPasses * kHistBins; i += kBigThreads)
-      w.hist[(size_t)r * kBigPasses * kHistBins + i] = 0u;
-  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
-  __shared__ uint32_t sh_and[kBigThreads / kWave], sh_or[kBigThreads / kWave];
-  __shared__ int sh_nan;
-  const float* row = a.scores + (size_t)r * a.ld;
-  uint32_t k[16], valid = 0u;
-  bool any_nan = false;
-  if (lo < hi) load_run16(row, lo, hi, k, &valid, &any_nan);   // else the identity is left
+  // Sample keys in registers (NaN as key 0; a slot past the row's end repeats the first key
+  // of its vector, which is inside the row), and the leading bits they all share.
+  uint32_t sk[4 * SV];
   uint32_t av = ~0u, ov = 0u;
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((valid >> e) & 1u) {
-      av &= k[e];
-      ov |= k[e];
+  for (int u = 0; u < SV; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool nn = false;
+      const uint32_t k = order_key(sv[u][e], nn);
+      sk[4 * u + e] = (e == 0 || 4 * si[u] + e < n) ? k : sk[4 * u];
+      av &= sk[4 * u + e];
+      ov |= sk[4 * u + e];
     }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     av &= (uint32_t)__shfl_xor((int)av, m);
     ov |= (uint32_t)__shfl_xor((int)ov, m);
   }
-  if (threadIdx.x == 0) sh_nan = 0;
+  if (lane == 0) { sh_and[wave] = av; sh_or[wave] = ov; }
   __syncthreads();
-  if (any_nan) sh_nan = 1;
-  if ((threadIdx.x & (kWave - 1)) == 0) { sh_and[threadIdx.x >> 6] = av; sh_or[threadIdx.x >> 6] = ov; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
-    w.ao[(size_t)r * chunks + blockIdx.x] = u32x4{av, ov, sh_nan ? 1u : 0u, 0u};
-  }
-}
-
-// Pass p: S_p (from the AND/OR prefix for p = 0, else by pick_digit from pass p - 1), then
-// this chunk's keys under the prefix P counted into pass p's histogram.
-__global__ __launch_bounds__(kBigThreads) void k_tkb_hist(TopkLaunch a, int chunks, int pass) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ int sh_scan[kBigThreads / kWave];
-  __shared__ int sh_sel[4];
-  const int r = blockIdx.y;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  BigState* slots = w.st + (size_t)r * kBigSlots;
-  uint32_t* hrow = w.hist + (size_t)r * kBigPasses * kHistBins;
-  BigState s;
-  if (pass == 0) {
-    int n0 = 0;
-    if (row_kind(a, r, &n0) != 0) return;
-    // the row's AND / OR / NaN from the per-chunk triples
-    __shared__ uint32_t sh_and[kBigThreads / kWave], sh_or[kBigThreads / kWave];
-    __shared__ uint32_t sh_nan[kBigThreads / kWave];
-    uint32_t av = ~0u, ov = 0u, nv = 0u;
-    for (int i = threadIdx.x; i < chunks; i += kBigThreads) {
-      const u32x4 v = w.ao[(size_t)r * chunks + i];
-      av &= v[0];
-      ov |= v[1];
-      nv |= v[2];
-    }
+  av = ~0u; ov = 0u;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      av &= (uint32_t)__shfl_xor((int)av, m);
-      ov |= (uint32_t)__shfl_xor((int)ov, m);
-      nv |= (uint32_t)__shfl_xor((int)nv, m);
-    }
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-      sh_and[threadIdx.x >> 6] = av; sh_or[threadIdx.x >> 6] = ov; sh_nan[threadIdx.x >> 6] = nv;
-    }
+  for (int i = 0; i < NW; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
+  // T: the leading bits of the rank-th largest sample key, 11 bits at a time below the
+  // shared ones, until its bucket holds at most rank / 2 sample keys or 22 bits are known;
+  // between rank and 1.5 rank sample keys are then >= T.  Every work-group of the row takes
+  // the same steps on the same keys, so all find the same T.
+  const int rank = min(kLongSample, (int)(1.5f * (float)a.top_k * (float)kLongSample / (float)n) + 16);
+  const uint32_t diff = av ^ ov;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known
+  uint32_t hm = shift >= 32 ? 0u : ~0u << shift;
+  uint32_t Pk = av & hm;
+  int need = rank;
+  while (shift > 10) {
+    const int wd = min(kMaxDigitBits, shift), nsh = shift - wd, nb = 1 << wd;
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
     __syncthreads();
-    for (int i = 0; i < kBigThreads / kWave; ++i) { av &= sh_and[i]; ov |= sh_or[i]; nv |= sh_nan[i]; }
-    s = BigState{av, ov, nv, 1u, 0ull, 0, 0, 0, 0, 0, 0};
-    const uint32_t diff = s.and_v ^ s.or_v;
-    s.shift = diff ? 32 - __builtin_clz(diff) : 0;
-    s.P = digit_prefix(s.and_v, s.shift);
-    s.need = a.top_k;
-    s.resolved = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && s.nan) raise_fault(a.fault, kFaultNan);
-  } else {
-    s = slots[pass - 1];
-    if (!s.active) return;
-    s = pick_digit(s, hrow + (size_t)(pass - 1) * kHistBins, sh_scan, sh_sel);
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) slots[pass] = s;
-  if (!refining(s)) return;
-  const int n = a.s.q_pos[r] + 1;
-  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
-  if (lo >= hi) return;
-  const int wd = min(kMaxDigitBits, s.shift), nsh = s.shift - wd, nb = 1 << wd;
-  for (int i = threadIdx.x; i < nb; i += kBigThreads) hist[i] = 0u;
-  __syncthreads();
-  const float* row = a.scores + (size_t)r * a.ld;
-  uint32_t k[16], valid;
-  bool any_nan;
-  load_run16(row, lo, hi, k, &valid, &any_nan);
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (((valid >> e) & 1u) && digit_prefix(k[e], s.shift) == s.P)
-      atomicAdd(&hist[(k[e] >> nsh) & (nb - 1)], 1u);
-  __syncthreads();
-  uint32_t* g = hrow + (size_t)pass * kHistBins;
-  for (int i = threadIdx.x; i < nb; i += kBigThreads)
-    if (hist[i]) atomicAdd(&g[i], hist[i]);
-}
+    for (int e = 0; e < 4 * SV; ++e)
+      if ((sk[e] & hm) == Pk) atomicAdd(&hist[(sk[e] >> nsh) & (nb - 1)], 1u);
+    __syncthreads();
+    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    const int d = sh_sel[0], abv = sh_sel[1], cnt = sh_sel[2];
+    __syncthreads();
+    Pk |= (uint32_t)d << nsh;
+    hm = ~0u << nsh;
+    need -= abv;
+    shift = nsh;
+    if (2 * cnt <= rank) break;
+  }
+  const uint32_t T = max(1u, Pk);
 
-// S_3 from the last pass's histogram, then this chunk's keys above / equal to the threshold.
-__global__ __launch_bounds__(kBigThreads) void k_tkb_count(TopkLaunch a, int chunks) {
-  __shared__ int sh_gt[kBigThreads / kWave], sh_eq[kBigThreads / kWave];
-  __shared__ int sh_scan[kBigThreads / kWave];
-  __shared__ int sh_sel[4];
-  const int r = blockIdx.y;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  BigState* slots = w.st + (size_t)r * kBigSlots;
-  BigState s = slots[kBigPasses - 1];
-  if (!s.active) return;
-  s = pick_digit(s, w.hist + ((size_t)r * kBigPasses + kBigPasses - 1) * kHistBins, sh_scan,
-                 sh_sel);
-  if (blockIdx.x == 0 && threadIdx.x == 0) slots[kBigPasses] = s;
-  const int shift = s.shift;
-  const uint64_t P = s.P;
-  const int n = a.s.q_pos[r] + 1;
-  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
-  const float* row = a.scores + (size_t)r * a.ld;
-  int gt = 0, eq = 0;
-  if (lo < hi) {
-    uint32_t k[16], valid;
-    bool any_nan;
-    load_run16(row, lo, hi, k, &valid, &any_nan);
+  uint32_t key[kLongEpt], sel = 0u;
+  bool nan = false;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if ((valid >> e) & 1u) {
-        const uint64_t h = digit_prefix(k[e], shift);
-        gt += h > P;
-        eq += h == P;
-      }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) { gt += __shfl_xor(gt, m); eq += __shfl_xor(eq, m); }
-  if ((threadIdx.x & (kWave - 1)) == 0) { sh_gt[threadIdx.x >> 6] = gt; sh_eq[threadIdx.x >> 6] = eq; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int G = 0, E = 0;
-    for (int i = 0; i < kBigThreads / kWave; ++i) { G += sh_gt[i]; E += sh_eq[i]; }
-    int* c = w.cnt + ((size_t)r * chunks + blockIdx.x) * 2;
-    c[0] = G;
-    c[1] = E;
-  }
-}
-
-__global__ __launch_bounds__(kBigThreads) void k_tkb_write(TopkLaunch a, int chunks) {
-  __shared__ int sh_scan[kBigThreads / kWave];
-  const int r = blockIdx.y;
-  BigWs w = big_ws(a.ws, a.s.total_q, chunks);
-  const BigState s = w.st[(size_t)r * kBigSlots + kBigPasses];
-  if (!s.active) return;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.len[r] = a.top_k;
-  const int shift = s.shift;
-  const uint64_t P = s.P;
-  const int n = a.s.q_pos[r] + 1;
-  const int lo = blockIdx.x * kBigChunk, hi = min(n, lo + kBigChunk);
-  if (lo >= hi) return;
-  // Keys above the threshold that precede this chunk, plus the equal keys taken before it:
-  // sums over the counts of the chunks before this one.
-  const int* c = w.cnt + (size_t)r * chunks * 2;
-  int g_sum = 0, e_sum = 0;
-  for (int i = threadIdx.x; i < (int)blockIdx.x; i += kBigThreads) {
-    g_sum += c[2 * i];
-    e_sum += c[2 * i + 1];
+  for (int e = 0; e < kLongEpt; ++e) {
+    bool nn = false;
+    key[e] = order_key(v[e >> 2][e & 3], nn);
+    if (t0 + e < hi) {
+      nan |= nn;
+      if (key[e] >= T) sel |= 1u << e;
+    }
   }
   int tot;
-  (void)block_exclusive_scan<kBigThreads>(g_sum, &tot, sh_scan);
-  const int gt_before = tot;
-  (void)block_exclusive_scan<kBigThreads>(e_sum, &tot, sh_scan);
-  const int eq_before = tot;
-  const int eq_taken_before = min(eq_before, s.need);
-  int carry_eq = eq_before, carry_out = gt_before + eq_taken_before;
-  const int K = a.top_k;
-  const float* row = a.scores + (size_t)r * a.ld;
-  int32_t* out = a.idx + (size_t)r * a.top_k;
-  // Thread i owns positions lo + 16 i .. +15, so thread order is position order: one scan
-  // ranks the equal keys, a second places the kept positions.
-  uint32_t k[16], valid;
-  bool any_nan;
-  load_run16(row, lo, hi, k, &valid, &any_nan);
-  uint32_t gt = 0u, eq = 0u;
+  int at = block_exclusive_scan<kRowThreads>(__builtin_popcount(sel), &tot, sh_scan);
+  const LongWs w = long_ws(a.ws, a.s.total_q, chunks);
+  u32x2* dst = w.list + ((size_t)r * chunks + c) * kLongChunk;
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((valid >> e) & 1u) {
-      const uint64_t h = digit_prefix(k[e], shift);
-      gt |= (h > P ? 1u : 0u) << e;
-      eq |= (h == P ? 1u : 0u) << e;
-    }
-  int eq_rank = carry_eq + block_exclusive_scan<kBigThreads>(__builtin_popcount(eq), &tot, sh_scan);
-  uint32_t sel = gt;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((eq >> e) & 1u) {
-      if (eq_rank < s.need) sel |= 1u << e;
-      ++eq_rank;
-    }
-  int at = carry_out + block_exclusive_scan<kBigThreads>(__builtin_popcount(sel), &tot, sh_scan);
-  const int t0 = lo + 16 * (int)threadIdx.x;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((sel >> e) & 1u) {
-      if (at < K) out[at] = t0 + e;
-      ++at;
-    }
+  for (int e = 0; e < kLongEpt; ++e)
+    if ((sel >> e) & 1u) dst[at++] = u32x2{key[e], (uint32_t)(t0 + e)};
+  if (tid == 0) w.cnt[(size_t)r * chunks + c] = tot;
+  if (__syncthreads_or(nan) && tid == 0) raise_fault(a.fault, kFaultNan);
 }
 
+__global__ __launch_bounds__(kRowThreads) void k_tkl_select(TopkLaunch a, int chunks) {
+  constexpr int NW = kRowThreads / kWave;
+  __shared__ int off[kMaxLongChunks + 1];
+  __shared__ __align__(16) int mark[kLongCand];
+  __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ int sh_scan[NW];
+  __shared__ int sh_sel[4];
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const LongWs w = long_ws(a.ws, a.s.total_q, chunks);
+  // every chunk's list length, loaded before the row is known (chunks past its end unused)
+  const int cnt_ld = tid < chunks ? w.cnt[(size_t)r * chunks + tid] : 0;
+  int n = 0;
+  if (!row_prologue(a, r, &n)) return;
+  const int K = a.top_k;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nch = (n + kLongChunk - 1) / kLongChunk;   // <= chunks <= kMaxLongChunks
+  const int mine = tid < nch ? cnt_ld : 0;
+  int m;
+  const int ex = block_exclusive_scan<kRowThreads>(mine, &m, sh_scan);
+  if (tid < nch) off[tid] = ex;
+  if (tid == nch - 1) off[nch] = ex + mine;
+  __syncthreads();
+  if (m < K || m > kLongCand) {   // threshold missed: exact selection over the whole row
+    row_select_exact<false>(a, r, n, nullptr);
+    return;
+  }
+
+  // Entries 16 tid .. 16 tid + 15 of the concatenated lists; key 0 marks an empty entry
+  // (every listed key is >= T >= 1).  Entry g of chunk c's list, which starts at entry
+  // off[c], sits at c * kLongChunk + (g - off[c]) = g + base(c), base(c) = c kLongChunk -
+  // off[c] non-decreasing in c (a list holds at most kLongChunk keys).  mark[g] holds base(c)
+  // where chunk c's (non-empty) list starts and 0 elsewhere, so an entry's base is the
+  // largest mark at or before it: thread tid finds the chunk of its first entry by binary
+  // search over off and carries the base forward.
+  for (int i = tid; i < m; i += kRowThreads) mark[i] = 0;
+  __syncthreads();
+  if (tid < nch && mine > 0) mark[ex] = tid * kLongChunk - ex;
+  __syncthreads();
+  const int g0 = kLongEpt * tid;
+  int base = 0;
+  u32x4 mk[kLongEpt / 4] = {};
+  if (g0 < m) {   // the last chunk c < nch with off[c] <= g0
+    int l = 0, h = nch - 1;
+    while (l < h) {
+      const int mid = (l + h + 1) >> 1;
+      if (off[mid] <= g0) l = mid; else h = mid - 1;
+    }
+    base = l * kLongChunk - off[l];
+#pragma unroll
+    for (int q = 0; q < kLongEpt / 4; ++q) mk[q] = *reinterpret_cast<const u32x4*>(mark + g0 + 4 * q);
+  }
+  const u32x2* lists = w.list + (size_t)r * chunks * kLongChunk;
+  uint32_t key[kLongEpt];
+  int pos[kLongEpt];
+#pragma unroll
+  for (int e = 0; e < kLongEpt; ++e) {
+    const int g = g0 + e;
+    const bool ok = g < m;   // entries past m read list entry 0 and are dropped
+    base = max(base, (int)mk[e >> 2][e & 3]);
+    const u32x2 x = lists[ok ? g + base : 0];
+    key[e] = ok ? x[0] : 0u;
+    pos[e] = (int)x[1];
+  }
+
+  // leading bits common to the list
+  uint32_t av = ~0u, ov = 0u;
+#pragma unroll
+  for (int e = 0; e < kLongEpt; ++e)
+    if (key[e]) { av &= key[e]; ov |= key[e]; }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    av &= (uint32_t)__shfl_xor((int)av, s);
+    ov |= (uint32_t)__shfl_xor((int)ov, s);
+  }
+  if (lane == 0) { sh_and[wave] = av; sh_or[wave] = ov; }
+  __syncthreads();
+  av = ~0u; ov = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
+  // The known leading bits as a mask and a masked key (32-bit compares on the 16 keys).
+  const uint32_t diff = av ^ ov;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known
+  uint32_t hm = shift >= 32 ? 0u : ~0u << shift;
+  uint32_t Pk = av & hm;
+  int need = K;
+  while (shift > 0) {
+    const int wd = min(kMaxDigitBits, shift), nsh = shift - wd, nb = 1 << wd;
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kLongEpt; ++e)
+      if (key[e] && (key[e] & hm) == Pk) atomicAdd(&hist[(key[e] >> nsh) & (nb - 1)], 1u);
+    __syncthreads();
+    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    const int d = sh_sel[0], abv = sh_sel[1], cnt = sh_sel[2];
+    __syncthreads();
+    Pk |= (uint32_t)d << nsh;
+    hm = ~0u << nsh;
+    need -= abv;
+    shift = nsh;
+    if (cnt == need) break;   // the whole bucket is selected
+  }
+
+  // kept positions in ascending order: entries are in position order across threads
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int e = 0; e < kLongEpt; ++e)
+    if (key[e]) {
+      const uint32_t h = key[e] & hm;
+      gt |= (h > Pk ? 1u : 0u) << e;
+      eq |= (h == Pk ? 1u : 0u) << e;
+    }
+  int tot;
+  int eq_rank = block_exclusive_scan<kRowThreads>(__builtin_popcount(eq), &tot, sh_scan);
+  uint32_t sel = gt;
+#pragma unroll
+  for (int e = 0; e < kLongEpt; ++e)
+    if ((eq >> e) & 1u) {
+      if (eq_rank < need) sel |= 1u << e;
+      ++eq_rank;
+    }
+  int at = block_exclusive_scan<kRowThreads>(__builtin_popcount(sel), &tot, sh_scan);
+  int32_t* out = a.idx + (size_t)r * K;
+#pragma unroll
+  for (int e = 0; e < kLongEpt; ++e)
+    if ((sel >> e) & 1u) {
+      if (at < K) out[at] = pos[e];
+      ++at;
+    }
+  if (tid == 0) a.len[r] = K;
+}
 
 }  // namespace
 
-static int big_chunks(const SeqView& s) { return (s.max_seq_len + kBigChunk - 1) / kBigChunk; }
+static int long_chunks(const SeqView& s) { return (s.max_seq_len + kLongChunk - 1) / kLongChunk; }
 
 size_t topk_ws_bytes(const SeqView& s, int top_k) {
   (void)top_k;
-  if (s.max_seq_len <= 4 * kCacheKeys) return 0;
-  const size_t rows = (size_t)s.total_q;
-  return round256(rows * kBigSlots * sizeof(BigState)) +
-         round256(rows * kBigPasses * kHistBins * 4) +
-         round256(rows * (size_t)big_chunks(s) * 2 * sizeof(int)) +
-         round256(rows * (size_t)big_chunks(s) * sizeof(u32x4));
+  if (s.max_seq_len <= kMaxCandRow) return 0;
+  const size_t rows = (size_t)s.total_q, chunks = (size_t)long_chunks(s);
+  return round256(rows * chunks * sizeof(int)) + rows * chunks * kLongChunk * sizeof(u32x2);
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
@@ -1040,13 +988,10 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
     k_topk_cand<<<s.total_q, kRowThreads, 0, st>>>(a);
     return hipGetLastError();
   }
-  const int chunks = big_chunks(s);
-  const dim3 grid(chunks, s.total_q);
-  k_tkb_andor<<<grid, kBigThreads, 0, st>>>(a, chunks);
-  for (int pass = 0; pass < kBigPasses; ++pass)
-    k_tkb_hist<<<grid, kBigThreads, 0, st>>>(a, chunks, pass);
-  k_tkb_count<<<grid, kBigThreads, 0, st>>>(a, chunks);
-  k_tkb_write<<<grid, kBigThreads, 0, st>>>(a, chunks);
+  const int chunks = long_chunks(s);
+  if (chunks > kMaxLongChunks) return hipErrorInvalidValue;
+  k_tkl_filter<<<dim3(s.total_q, chunks), kRowThreads, 0, st>>>(a, chunks);
+  k_tkl_select<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
   return hipGetLastError();
 }
 

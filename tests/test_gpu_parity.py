@@ -245,17 +245,21 @@ def test_topk_long_rows_of_mixed_lengths():
 
 
 @pytest.mark.parametrize("n,top_k,kind", [(20000, 2048, "const"), (50000, 2048, "tie_block"),
-                                          (9000, 2048, "const")])
+                                          (9000, 2048, "const"), (200000, 2048, "const"),
+                                          (300000, 2048, "tie_block"),
+                                          (300000, 2048, "tie_block_20k")])
 def test_topk_when_the_candidate_list_overflows(n, top_k, kind):
     """Rows whose keys above the sampled threshold do not fit the candidate list (massive
-    ties at the threshold) take the streaming selection; the result is still the oracle's."""
+    ties at the threshold) take the streaming selection; the result is still the oracle's.
+    On long rows 9,000 tied keys fit the list (ties resolved in it, lowest positions
+    first) and 20,000 do not."""
     _say(f"[gpu] topk overflow n={n} k={top_k} {kind}")
     g = torch.Generator().manual_seed(n)
     if kind == "const":
         x = torch.full((n,), 0.25)
     else:
         x = torch.clamp(torch.randn(n, generator=g), max=2.9)
-        x[torch.randperm(n, generator=g)[:9000]] = 3.0
+        x[torch.randperm(n, generator=g)[:20000 if kind == "tie_block_20k" else 9000]] = 3.0
     ld = (n + 3) // 4 * 4
     scores = torch.full((1, ld), -5.0)
     scores[0, :n] = x
@@ -272,6 +276,38 @@ def test_topk_when_the_candidate_list_overflows(n, top_k, kind):
     oi, on = O.topk_row(scores.numpy()[0].astype(np.float64), n - 1, top_k)
     assert t_np(ln)[0] == on
     assert np.array_equal(t_np(idx)[0], oi)
+
+
+def test_topk_long_row_whose_sample_overestimates_the_threshold():
+    """A long row built so that the threshold taken from its sample keeps fewer than k keys:
+    the row's sample slots (2,048 float4 vectors at (j * n4) // 2,048, j < 2,048; white-box
+    knowledge of the long-row filter) start with a large key, one of them is left out, so
+    2,047 keys lie above every other key and the sample's rank-k-scaled key is one of them.
+    The selection must notice the short list and fall back; the result is the oracle's."""
+    n, top_k = 300000, 2048
+    _say(f"[gpu] topk long-row sample miss n={n} k={top_k}")
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(n, generator=g)
+    n4 = (n + 3) // 4
+    slots = torch.tensor([4 * ((j * n4) // 2048) for j in range(1, 2048)])
+    x[slots] = 10.0
+    ld = (n + 3) // 4 * 4
+    scores = torch.full((1, ld), -5.0)
+    scores[0, :n] = x
+    batch = synth.make_batch(2, [n], [1], 64, device=DEV)
+    seqs = M.make_seqs(batch)
+    idx = torch.full((1, top_k), -9, dtype=torch.int32, device=DEV)
+    ln = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_TOPK, seqs, 0, top_k)
+    ws = torch.empty(max(wsn, 256), dtype=torch.uint8, device=DEV)
+    fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+    M.ml4_topk_select(seqs, scores.to(DEV), ld, top_k, idx, ln, ws, wsn, fault)
+    torch.cuda.synchronize()
+    assert M.ml4_fault_query(fault) == 0
+    oi, on = O.topk_row(scores.numpy()[0].astype(np.float64), n - 1, top_k)
+    assert t_np(ln)[0] == on
+    assert np.array_equal(t_np(idx)[0], oi)
+    assert set(slots.tolist()) <= set(t_np(idx)[0].tolist())
 
 
 def _topk_lists(case, seed, top_k):

@@ -41,8 +41,8 @@ def _bytes(t):
 
 def test_static_scratch_entry_matches_workspace_entry_on_two_calls():
     L = synth.layer_desc
-    # first call: two rows past 131,072 positions (the multi-work-group top-k passes keep
-    # their histograms, states and counts in the scratch) and few rows (split-MLA partials
+    # first call: two rows past 131,072 positions (the long-row top-k keeps its per-chunk
+    # candidate lists and their lengths in the scratch) and few rows (split-MLA partials
     # in the scratch), owner / shared-indexer / consumer layers
     big = synth.make_case(
         "na_big", 91, seq_lens=[140001, 150000], q_per_seq=[1, 1], block_size=64, fmt="fp8",
