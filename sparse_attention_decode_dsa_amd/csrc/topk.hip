@@ -692,10 +692,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
 // ------------------------------------------------- long rows: chunk filters, then one select
 // Rows above 131,072 positions, two launches.
 // 1. k_tkl_filter, one work-group per 16,384-position chunk of a row: every work-group of the
-//    row takes the same threshold T from the same 8,192-key sample (the candidate filter's
-//    rule, here rank ~1.5 K n_s / n + 16 to 22 leading bits, and T >= 1 so that NaN never
-//    passes), then writes the chunk's keys >= T with their positions, in position order, to
-//    the chunk's own list, and the list's length.
+//    row takes the same threshold T from the same sample (8,192 keys for rows up to 2M
+//    positions, 16,384 up to 4M, 32,768 beyond) by the same steps (T >= 1, so that NaN
+//    never passes), then writes the chunk's keys >= T with their positions, in position
+//    order, to the chunk's own list, and the list's length.
 // 2. k_tkl_select, one work-group per row: the chunk lists taken in chunk order are the row's
 //    keys >= T in position order.  With at least K and at most kLongCand of them, the top K
 //    of the row are the top K of the list: thread i holds entries 16 i .. 16 i + 15 in
@@ -705,7 +705,6 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
 constexpr int kLongEpt = 16;                          // keys per thread in both launches
 constexpr int kLongChunk = kLongEpt * kRowThreads;    // 16,384 positions per filter work-group
 constexpr int kLongCand = kLongEpt * kRowThreads;     // longest list the select holds
-constexpr int kLongSample = 8192;                     // sample keys: two float4 per thread
 constexpr int kMaxLongChunks = kRowThreads;           // one chunk length per select thread
 
 struct LongWs {
@@ -723,9 +722,9 @@ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int chunks) {
   return w;
 }
 
+template <int SU>
 __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int chunks) {
   constexpr int NW = kRowThreads / kWave;
-  constexpr int SV = kLongSample / 4 / kRowThreads;   // sample float4 per thread
   __shared__ uint32_t hist[1 << kMaxDigitBits];
   __shared__ int sh_scan[NW];
   __shared__ int sh_sel[4];
@@ -747,20 +746,22 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
   for (int j = 0; j < kLongEpt / 4; ++j)
     v[j] = t0 + 4 * j < hi ? *reinterpret_cast<const f32x4*>(row + t0 + 4 * j)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
-  int si[SV];
-  f32x4 sv[SV];
+  // The sample: ns = 4,096 SU keys spread over the row (SU float4 per thread).
+  constexpr int ns = kRowThreads * 4 * SU;
+  int si[SU];
+  f32x4 sv[SU];
 #pragma unroll
-  for (int u = 0; u < SV; ++u) {
+  for (int u = 0; u < SU; ++u) {
     const int j = tid + kRowThreads * u;
-    si[u] = (int)(((long long)j * n4) / (kLongSample / 4));
+    si[u] = (int)(((long long)j * n4) / (ns / 4));
     sv[u] = *reinterpret_cast<const f32x4*>(row + 4 * si[u]);
   }
   // Sample keys in registers (NaN as key 0; a slot past the row's end repeats the first key
   // of its vector, which is inside the row), and the leading bits they all share.
-  uint32_t sk[4 * SV];
+  uint32_t sk[4 * SU];
   uint32_t av = ~0u, ov = 0u;
 #pragma unroll
-  for (int u = 0; u < SV; ++u)
+  for (int u = 0; u < SU; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       bool nn = false;
@@ -780,10 +781,14 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
 #pragma unroll
   for (int i = 0; i < NW; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
   // T: the leading bits of the rank-th largest sample key, 11 bits at a time below the
-  // shared ones, until its bucket holds at most rank / 2 sample keys or 22 bits are known;
-  // between rank and 1.5 rank sample keys are then >= T.  Every work-group of the row takes
-  // the same steps on the same keys, so all find the same T.
-  const int rank = min(kLongSample, (int)(1.5f * (float)a.top_k * (float)kLongSample / (float)n) + 16);
+  // shared ones, until the sample keys >= T predict at most half a full list for the row
+  // (or 22 bits are known).  rank ~1.5 K ns / n + 16, held to a predicted 0.45 of a full
+  // list.  Every work-group of the row takes the same steps on the same keys, so all find
+  // the same T.
+  const float scale = (float)ns / (float)n;
+  const int rank = max(1, min((int)(1.5f * (float)a.top_k * scale) + 16,
+                              (int)(0.45f * (float)kLongCand * scale)));
+  const int lim = (int)(0.5f * (float)kLongCand * scale);
   const uint32_t diff = av ^ ov;
   int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known
   uint32_t hm = shift >= 32 ? 0u : ~0u << shift;
@@ -794,7 +799,7 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
     for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4 * SV; ++e)
+    for (int e = 0; e < 4 * SU; ++e)
       if ((sk[e] & hm) == Pk) atomicAdd(&hist[(sk[e] >> nsh) & (nb - 1)], 1u);
     __syncthreads();
     find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
@@ -804,7 +809,7 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
     hm = ~0u << nsh;
     need -= abv;
     shift = nsh;
-    if (2 * cnt <= rank) break;
+    if (rank - need + cnt <= lim) break;   // sample keys >= T
   }
   const uint32_t T = max(1u, Pk);
 
@@ -990,7 +995,14 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   }
   const int chunks = long_chunks(s);
   if (chunks > kMaxLongChunks) return hipErrorInvalidValue;
-  k_tkl_filter<<<dim3(s.total_q, chunks), kRowThreads, 0, st>>>(a, chunks);
+  // sample float4 per thread: 2 up to 2M positions, 4 up to 4M, 8 beyond
+  const dim3 grid(s.total_q, chunks);
+  if (s.max_seq_len <= (2 << 20))
+    k_tkl_filter<2><<<grid, kRowThreads, 0, st>>>(a, chunks);
+  else if (s.max_seq_len <= (4 << 20))
+    k_tkl_filter<4><<<grid, kRowThreads, 0, st>>>(a, chunks);
+  else
+    k_tkl_filter<8><<<grid, kRowThreads, 0, st>>>(a, chunks);
   k_tkl_select<<<s.total_q, kRowThreads, 0, st>>>(a, chunks);
   return hipGetLastError();
 }

@@ -244,6 +244,35 @@ def test_topk_long_rows_of_mixed_lengths():
             assert np.array_equal(gi[r], oi), f"call {call} row {r}: first diff at {np.argmax(gi[r] != oi)}"
 
 
+def test_topk_rows_of_millions_of_positions():
+    """Rows of 3,000,001 and 6,500,000 positions in one launch (the long-row filter's sample
+    grows with the row: 16,384 and 32,768 keys), one of them with many ties: the selected
+    sets equal the oracle's."""
+    lens = [3000001, 6500000]
+    top_k = 2048
+    _say(f"[gpu] topk rows of millions {lens} k={top_k}")
+    ld = (max(lens) + 3) // 4 * 4
+    scores = torch.full((len(lens), ld), -5.0)
+    for i, n in enumerate(lens):
+        scores[i, :n] = _rand_scores(n, 4100 + i, dup_levels=[None, 64][i])
+    batch = synth.make_batch(78, lens, [1] * len(lens), 64, device=DEV)
+    seqs = M.make_seqs(batch)
+    wsn = M.ml4_workspace_bytes(M.ML4_ENTRY_TOPK, seqs, 0, top_k)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    idx = torch.full((len(lens), top_k), -9, dtype=torch.int32, device=DEV)
+    ln = torch.zeros(len(lens), dtype=torch.int32, device=DEV)
+    fault = torch.zeros(1, dtype=torch.int32, device=DEV)
+    M.ml4_topk_select(seqs, scores.to(DEV), ld, top_k, idx, ln, ws, wsn, fault)
+    torch.cuda.synchronize()
+    assert M.ml4_fault_query(fault) == 0
+    gi, gl = t_np(idx), t_np(ln)
+    pos = t_np(batch.q_pos)
+    for r in range(len(lens)):
+        oi, on = O.topk_row(scores[r].numpy().astype(np.float64), int(pos[r]), top_k)
+        assert gl[r] == on
+        assert np.array_equal(gi[r], oi), f"row {r}: first diff at {np.argmax(gi[r] != oi)}"
+
+
 @pytest.mark.parametrize("n,top_k,kind", [(20000, 2048, "const"), (50000, 2048, "tie_block"),
                                           (9000, 2048, "const"), (200000, 2048, "const"),
                                           (300000, 2048, "tie_block"),
