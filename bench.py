@@ -396,6 +396,22 @@ def achievable_peaks(dev: str):
     return out
 
 
+def mla_two_groups(rows, heads, top_k):
+    """Whether the library runs fp8_ds_mla rows in its 64-head (two wave group) form: at
+    most 64 heads, or when 128-head work-groups, split over keys (>= 4 tiles of 32 keys per
+    split, splits doubled while the grid is under 256 work-groups), would still number
+    under 256.  Mirrors the library's dispatch; used to name the kernel in reports."""
+    if heads <= 64:
+        return True
+    groups = (heads + 127) // 128
+    max_split = max(1, (top_k + 127) // 128)
+    ns = 1
+    while ns < max_split and rows * groups * ns < 256:
+        ns <<= 1
+    ns = min(ns, max_split)
+    return rows * groups * ns < 256
+
+
 def kernel_report(work, per, layers, case, T, ach):
     """Each kernel of each layer against its floors: HBM bytes at 8 TB/s, FP8 FLOPs at
     5.0 and 16-bit FLOPs at 2.5 PFLOP/s (datasheet), and the same against the measured
@@ -634,10 +650,10 @@ def main():
             roof["kernel"] = {"indexer": "k_indexer_f32", "mla": "k_mla_f32",
                               "topk": "k_topk_cand"}[dom]
         else:
-            # k_mla_fp8<rope, format, two wave groups (<= 64 heads)>
+            # k_mla_fp8<rope, format, two wave groups>
+            tg = mla_two_groups(T, case.mla_heads, case.layers[0]["top_k"])
             roof["kernel"] = {"indexer": "k_indexer_fp8",
-                              "mla": "k_mla_fp8<%d, 0, %s>" % (
-                                  rope0, "true" if case.mla_heads <= 64 else "false"),
+                              "mla": "k_mla_fp8<%d, 0, %s>" % (rope0, "true" if tg else "false"),
                               "topk": "k_topk_cand"}[dom]
         roof["layer"] = l0
         roof["avg_launch_us"] = us
