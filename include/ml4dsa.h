@@ -143,7 +143,9 @@ int ml4_indexer_score(const ml4_seqs* s, const ml4_cache* idx_cache, const void*
  *   -0 == +0; NaN ranks below -inf (and sets ML4_FAULT_NAN_SCORE).
  *   topk_idx [total_q][top_k] int32: the selected positions in ascending t, then -1.
  *   topk_len [total_q] int32 = min(top_k, q_pos[r] + 1).
- *   1 <= top_k <= 2048.  ws: ml4_workspace_bytes(ML4_ENTRY_TOPK, ...) bytes (may be 0).
+ *   1 <= top_k <= 2048.  ws: ml4_workspace_bytes(ML4_ENTRY_TOPK, ...) bytes: 0 when
+ *   max_seq_len <= 131,072, else per-chunk candidate lists (8 bytes per position and row
+ *   plus a length per 16,384 positions and row), written before they are read.
  * Integer work on the order-preserving u32 image of each fp32 score: deterministic.
  */
 int ml4_topk_select(const ml4_seqs* s, const float* scores, int64_t ld_scores, int32_t top_k,
@@ -277,9 +279,9 @@ int ml4_sparse_attn_layer(const ml4_layer* layers, int32_t layer, const ml4_seqs
  * ml4_sparse_attn_layer_static -- ml4_sparse_attn_layer without a workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  It allocates nothing: the scratch (scores,
- * top-k passes, split-MLA partials) is one fixed device array of ML4_STATIC_SCRATCH_BYTES
- * inside the library, which each GPU the library runs on holds from the library's first
- * use on it until the process ends.
+ * top-k candidate lists, split-MLA partials) is one fixed device array of
+ * ML4_STATIC_SCRATCH_BYTES inside the library, which each GPU the library runs on holds
+ * from the library's first use on it until the process ends.
  *   Arguments, results, validation and fault bits as ml4_sparse_attn_layer.
  *   A batch whose ml4_workspace_bytes(ML4_ENTRY_LAYER, ...) exceeds ML4_STATIC_SCRATCH_BYTES
  *   is refused with ML4_E_UNSUPPORTED (nothing launched); 64 MiB holds the scores of
