@@ -783,11 +783,11 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
   // T: the leading bits of the rank-th largest sample key, 11 bits at a time below the
   // shared ones, until the sample keys >= T predict at most half a full list for the row
   // (or 22 bits are known).  rank ~1.5 K ns / n + 16, held to a predicted 0.45 of a full
-  // list.  Every work-group of the row takes the same steps on the same keys, so all find
+  // list and to the sample's size (a short row of a long-row launch).  Every work-group of the row takes the same steps on the same keys, so all find
   // the same T.
   const float scale = (float)ns / (float)n;
-  const int rank = max(1, min((int)(1.5f * (float)a.top_k * scale) + 16,
-                              (int)(0.45f * (float)kLongCand * scale)));
+  const int rank = max(1, min(ns, min((int)(1.5f * (float)a.top_k * scale) + 16,
+                                      (int)(0.45f * (float)kLongCand * scale))));
   const int lim = (int)(0.5f * (float)kLongCand * scale);
   const uint32_t diff = av ^ ov;
   int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known

@@ -210,17 +210,18 @@ def test_topk_exact_on_given_scores(n, top_k, seed):
 def test_topk_long_rows_of_mixed_lengths():
     """The multi-work-group selection (rows above 131,072 positions) with rows of unequal
     length in one launch: a row shorter than k (returned whole), one in the one-work-group
-    range and long rows whose chunk counts differ, so some work-groups of the grid have no
-    keys of their row; every row equals the oracle's, and a second call on the same
-    workspace gives the same result."""
-    lens = [140000, 1500, 200003, 70000, 131073]
+    range, long rows whose chunk counts differ (so some work-groups of the grid have no
+    keys of their row) and a row of 2,500 positions (fewer than the long-row sample's rank
+    would ask for); every row equals the oracle's, and a second call on the same workspace
+    gives the same result."""
+    lens = [140000, 1500, 200003, 70000, 131073, 2500]
     top_k = 2048
     _say(f"[gpu] topk mixed long rows {lens} k={top_k}")
     n_max = max(lens)
     ld = (n_max + 3) // 4 * 4
     scores = torch.full((len(lens), ld), -5.0)
     for i, n in enumerate(lens):
-        x = _rand_scores(n, 900 + i, dup_levels=[None, 4, 16, None, 2][i])
+        x = _rand_scores(n, 900 + i, dup_levels=[None, 4, 16, None, 2, None][i])
         scores[i, :n] = x
     batch = synth.make_batch(77, lens, [1] * len(lens), 64, device=DEV)
     seqs = M.make_seqs(batch)
