@@ -459,8 +459,60 @@ __device__ void finish_from_candidates(const TopkLaunch& a, int r, int n, const 
   if (tid == 0) a.len[r] = K;
 }
 
+// Threshold of a candidate filter from a sample held NK keys per thread (every thread of a
+// kRowThreads work-group calls it): the leading bits of the rank-th largest sample key,
+// 11 bits at a time below the bits every sample key shares, until the sample keys >= T
+// number at most lim (or 22 bits are known); the bits below are left clear.  rank must not
+// exceed the sample's size.
+template <int NK>
+__device__ uint32_t sample_threshold(const uint32_t (&sk)[NK], int rank, int lim, uint32_t* hist,
+                                     int* sh_scan, int* sh_sel, uint32_t* sh_and, uint32_t* sh_or) {
+  constexpr int NW = kRowThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  uint32_t av = ~0u, ov = 0u;
+#pragma unroll
+  for (int e = 0; e < NK; ++e) {
+    av &= sk[e];
+    ov |= sk[e];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    av &= (uint32_t)__shfl_xor((int)av, m);
+    ov |= (uint32_t)__shfl_xor((int)ov, m);
+  }
+  if (lane == 0) { sh_and[wave] = av; sh_or[wave] = ov; }
+  __syncthreads();
+  av = ~0u; ov = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
+  const uint32_t diff = av ^ ov;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known
+  uint32_t hm = shift >= 32 ? 0u : ~0u << shift;
+  uint32_t Pk = av & hm;
+  int need = rank;
+  while (shift > 10) {
+    const int wd = min(kMaxDigitBits, shift), nsh = shift - wd, nb = 1 << wd;
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NK; ++e)
+      if ((sk[e] & hm) == Pk) atomicAdd(&hist[(sk[e] >> nsh) & (nb - 1)], 1u);
+    __syncthreads();
+    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
+    const int d = sh_sel[0], abv = sh_sel[1], cnt = sh_sel[2];
+    __syncthreads();
+    Pk |= (uint32_t)d << nsh;
+    hm = ~0u << nsh;
+    need -= abv;
+    shift = nsh;
+    if (rank - need + cnt <= lim) break;   // sample keys >= T
+  }
+  return Pk;
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
   constexpr int NW = kRowThreads / kWave;
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
   __shared__ uint32_t cand_key[kCand];
   __shared__ int cand_t[kCand];
   __shared__ uint32_t sel_bits[kMaxCandRow / 32], tie_bits[kMaxCandRow / 32];
@@ -487,23 +539,23 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
     first[u] = i4 < n4 ? *reinterpret_cast<const f32x4*>(row + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // 1. threshold (22 leading bits are enough; the low 10 are left clear)
+  // 1. threshold: the sample's rank-th key to as many leading bits as keep the list short
   uint32_t T = 0u;
   if (n > kCand) {
-    const int j = tid;   // one float4 per thread
-    const int i4 = (int)(((long long)j * n4) / kSampleVec);
+    const int i4 = (int)(((long long)tid * n4) / kSampleVec);   // one float4 per thread
     const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * i4);
+    uint32_t sk[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; ++e) {   // a slot past the row's end repeats the vector's first key
       bool nn = false;
       const uint32_t k = order_key(v[e], nn);
-      cand_key[4 * j + e] = (4 * i4 + e < n) ? k : 0u;
+      sk[e] = (e == 0 || 4 * i4 + e < n) ? k : sk[0];
     }
-    __syncthreads();
-    const int ns = 4 * kSampleVec;
-    const int rank = min(ns, (int)(1.5f * (float)K * (float)ns / (float)n) + 8);
-    int above;
-    T = lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel, 10);
+    constexpr int ns = 4 * kSampleVec;
+    const float scale = (float)ns / (float)n;
+    const int rank = min(ns, (int)(1.5f * (float)K * scale) + 8);
+    T = sample_threshold(sk, rank, (int)(0.5f * (float)kCand * scale), hist, sh_scan, sh_sel,
+                         sh_and, sh_or);
   }
 
   // 2. candidate list
@@ -587,11 +639,14 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_cand(TopkLaunch a) {
 // overlaps the tail of its transfer.  The sample: each thread's vector tid % V (4,096 keys
 // spread over the row).  A list that misses (fewer than K keys or more than kCandReg) falls
 // back to the streaming exact selection.
-constexpr int kCandReg = 4096;
-
-template <int V>
+// ADAPT (launches of at most one work-group per CU, where a row's latency is the step's):
+// the threshold stops refining once the sample predicts at most half a full list, over a
+// list of 8,192 keys; otherwise (many rows, throughput) 22 bits over a list of 4,096.
+template <int V, bool ADAPT>
 __global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
   constexpr int NW = kRowThreads / kWave;
+  constexpr int kCandReg = ADAPT ? 8192 : 4096;
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
   constexpr int WPT = V >= 8 ? V / 8 : 1;        // bitmap words per thread (n / 32 words)
   __shared__ uint32_t cand_key[kCandReg];
   __shared__ int cand_t[kCandReg];
@@ -644,13 +699,19 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_reg(TopkLaunch a) {
 #pragma unroll
     for (int j = 1; j < V; ++j)
       if (j == js) { sk[0] = key[j][0]; sk[1] = key[j][1]; sk[2] = key[j][2]; sk[3] = key[j][3]; }
+    constexpr int ns = 4 * kRowThreads;
+    const float scale = (float)ns / (float)n;
+    const int rank = min(ns, (int)(1.5f * (float)K * scale) + 8);
+    if constexpr (ADAPT) {
+      T = max(1u, sample_threshold(sk, rank, (int)(0.5f * (float)kCandReg * scale), hist, sh_scan,
+                                   sh_sel, sh_and, sh_or));
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cand_key[4 * tid + e] = sk[e];
-    __syncthreads();
-    const int ns = 4 * kRowThreads;
-    const int rank = min(ns, (int)(1.5f * (float)K * (float)ns / (float)n) + 8);
-    int above;
-    T = max(1u, lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel, 10));
+      for (int e = 0; e < 4; ++e) cand_key[4 * tid + e] = sk[e];
+      __syncthreads();
+      int above;
+      T = max(1u, lds_select(cand_key, ns, rank, &above, hist, sh_scan, sh_sel, 10));
+    }
   }
   __syncthreads();
 
@@ -735,7 +796,6 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
   const int lo = c * kLongChunk, hi = min(n, lo + kLongChunk);
   if (lo >= hi) return;                  // past this row's end: the select reads no list here
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid >> 6;
   const float* row = a.scores + (size_t)r * a.ld;
   const int n4 = (n + 3) >> 2;
   // The chunk's 16 keys per thread and the sample's vectors, all loads in flight at once.
@@ -757,9 +817,8 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
     sv[u] = *reinterpret_cast<const f32x4*>(row + 4 * si[u]);
   }
   // Sample keys in registers (NaN as key 0; a slot past the row's end repeats the first key
-  // of its vector, which is inside the row), and the leading bits they all share.
+  // of its vector, which is inside the row).
   uint32_t sk[4 * SU];
-  uint32_t av = ~0u, ov = 0u;
 #pragma unroll
   for (int u = 0; u < SU; ++u)
 #pragma unroll
@@ -767,50 +826,16 @@ __global__ __launch_bounds__(kRowThreads) void k_tkl_filter(TopkLaunch a, int ch
       bool nn = false;
       const uint32_t k = order_key(sv[u][e], nn);
       sk[4 * u + e] = (e == 0 || 4 * si[u] + e < n) ? k : sk[4 * u];
-      av &= sk[4 * u + e];
-      ov |= sk[4 * u + e];
     }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    av &= (uint32_t)__shfl_xor((int)av, m);
-    ov |= (uint32_t)__shfl_xor((int)ov, m);
-  }
-  if (lane == 0) { sh_and[wave] = av; sh_or[wave] = ov; }
-  __syncthreads();
-  av = ~0u; ov = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) { av &= sh_and[i]; ov |= sh_or[i]; }
-  // T: the leading bits of the rank-th largest sample key, 11 bits at a time below the
-  // shared ones, until the sample keys >= T predict at most half a full list for the row
-  // (or 22 bits are known).  rank ~1.5 K ns / n + 16, held to a predicted 0.45 of a full
-  // list and to the sample's size (a short row of a long-row launch).  Every work-group of the row takes the same steps on the same keys, so all find
-  // the same T.
+  // T: until the sample keys >= T predict at most half a full list for the row; rank ~1.5 K
+  // ns / n + 16, held to a predicted 0.45 of a full list and to the sample's size (a short
+  // row of a long-row launch).  Every work-group of the row takes the same steps on the
+  // same keys, so all find the same T.
   const float scale = (float)ns / (float)n;
   const int rank = max(1, min(ns, min((int)(1.5f * (float)a.top_k * scale) + 16,
                                       (int)(0.45f * (float)kLongCand * scale))));
-  const int lim = (int)(0.5f * (float)kLongCand * scale);
-  const uint32_t diff = av ^ ov;
-  int shift = diff ? 32 - __builtin_clz(diff) : 0;   // bits >= shift are known
-  uint32_t hm = shift >= 32 ? 0u : ~0u << shift;
-  uint32_t Pk = av & hm;
-  int need = rank;
-  while (shift > 10) {
-    const int wd = min(kMaxDigitBits, shift), nsh = shift - wd, nb = 1 << wd;
-    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 4 * SU; ++e)
-      if ((sk[e] & hm) == Pk) atomicAdd(&hist[(sk[e] >> nsh) & (nb - 1)], 1u);
-    __syncthreads();
-    find_digit<kRowThreads>(hist, nb, need, sh_sel, sh_scan);
-    const int d = sh_sel[0], abv = sh_sel[1], cnt = sh_sel[2];
-    __syncthreads();
-    Pk |= (uint32_t)d << nsh;
-    hm = ~0u << nsh;
-    need -= abv;
-    shift = nsh;
-    if (rank - need + cnt <= lim) break;   // sample keys >= T
-  }
+  const uint32_t Pk = sample_threshold(sk, rank, (int)(0.5f * (float)kLongCand * scale), hist,
+                                       sh_scan, sh_sel, sh_and, sh_or);
   const uint32_t T = max(1u, Pk);
 
   uint32_t key[kLongEpt], sel = 0u;
@@ -983,10 +1008,14 @@ size_t topk_ws_bytes(const SeqView& s, int top_k) {
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t st) {
   const SeqView& s = a.s;
   if (s.max_seq_len <= 4 * kRowThreads * 8) {
-    if (s.max_seq_len <= 4 * kRowThreads * 4)
-      k_topk_reg<4><<<s.total_q, kRowThreads, 0, st>>>(a);
-    else
-      k_topk_reg<8><<<s.total_q, kRowThreads, 0, st>>>(a);
+    const bool adapt = s.total_q <= 256;   // at most one work-group per CU
+    if (s.max_seq_len <= 4 * kRowThreads * 4) {
+      if (adapt) k_topk_reg<4, true><<<s.total_q, kRowThreads, 0, st>>>(a);
+      else k_topk_reg<4, false><<<s.total_q, kRowThreads, 0, st>>>(a);
+    } else {
+      if (adapt) k_topk_reg<8, true><<<s.total_q, kRowThreads, 0, st>>>(a);
+      else k_topk_reg<8, false><<<s.total_q, kRowThreads, 0, st>>>(a);
+    }
     return hipGetLastError();
   }
   if (s.max_seq_len <= kMaxCandRow) {
